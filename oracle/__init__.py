@@ -1,0 +1,209 @@
+"""Plain fp64 CPU oracle for draft-tree verification -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never imports, links or executes anything here, and this package
+imports nothing from the product.
+
+The arithmetic lives in ``tev_oracle.c`` (plain loops, double precision,
+optional OpenMP over independent rows); this module only marshals numpy
+arrays.  Sources:
+
+* "Where Draft Trees Lose Target Mass: Exit-Guided Speculative Decoding"
+  (arXiv 2610.11750): Sec. 3 Eq. 1-2 (p_v, reach P), Sec. 3.1 Eq. 4 (A(v),
+  rho, w), Lemma 1 Eq. 5, Sec. 3.2 Eq. 6 (coverage), Eq. 7 (residual law),
+  App. B Algorithm 1 (TEV's two draws).
+* "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
+  (arXiv 2610.00321): App. B Lemma 1 and App. C "Packed verification"
+  (ancestor-only attention mask).
+
+Parity pins live in ``tests/test_oracle_*.py``.  Every function here is pinned
+(see those tests); none is "parity unpinned" except the exact index a given
+uniform maps to, which no page prints and which follows from the inverse-CDF
+reading together with the enumerated law.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tev_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+_DTYPE_CODES = {"f32": F32, "bf16": BF16, "f64": F64}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP)."""
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-Werror", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, ip, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.oracle_exit_law.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, vp, vp, vp, ip]
+        lib.oracle_sample.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, ip, vp, vp, vp, ip]
+        lib.oracle_residual_cdf.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp]
+        lib.oracle_tree_attn.argtypes = [vp, vp, vp, ip, vp, ip, ip, ip, ip, ip, ip, dp, vp, vp,
+                                         ctypes.c_int64, ip]
+        lib.oracle_check_tree.argtypes = [vp, vp, ip, ip]
+        lib.oracle_max_threads.argtypes = [ip]
+        for f in ("oracle_exit_law", "oracle_sample", "oracle_residual_cdf", "oracle_tree_attn",
+                  "oracle_check_tree", "oracle_max_threads"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_input(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Contiguous view with the element type the C widening expects."""
+    want = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}[dtype]
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError(f"expected {want} storage for dtype {dtype}, got {x.dtype}")
+    return x
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def max_threads(nthreads: int = 0) -> int:
+    return int(_load().oracle_max_threads(int(nthreads)))
+
+
+def check_tree(parents: np.ndarray, tokens: np.ndarray, V: int) -> bool:
+    p = np.ascontiguousarray(parents, dtype=np.int32)
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return _load().oracle_check_tree(_ptr(p), _ptr(t), int(p.shape[-1]), int(V)) == 0
+
+
+@dataclass
+class ExitLaw:
+    rho: np.ndarray        # [R][B]
+    reach: np.ndarray      # [R][B]
+    exit_mass: np.ndarray  # [R][B]
+    coverage: np.ndarray   # [R]
+    logZ: np.ndarray       # [R][B]
+
+
+def exit_law(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
+             inv_temperature: float = 1.0, nthreads: int = 0) -> ExitLaw:
+    """rho, P, w, C of 2610.11750 Sec. 3 (Eq. 2, 4, 6) per request.
+
+    ``logits`` has shape [R][B][V] (or [B][V] for one request) and storage
+    float32 (dtype "f32"), uint16 bf16 bits ("bf16") or float64 ("f64").
+    """
+    lg = _as_input(logits, dtype)
+    if lg.ndim == 2:
+        lg = lg[None]
+    R, B, V = lg.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(R, B)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(R, B)
+    rho = np.empty((R, B)); reach = np.empty((R, B)); w = np.empty((R, B))
+    cov = np.empty(R); logZ = np.empty((R, B))
+    st = _load().oracle_exit_law(_ptr(lg), _DTYPE_CODES[dtype], _ptr(par), _ptr(tok), R, B, V,
+                                 float(inv_temperature), _ptr(rho), _ptr(reach), _ptr(w),
+                                 _ptr(cov), _ptr(logZ), int(nthreads))
+    if st != 0:
+        raise OracleError(f"oracle_exit_law failed with status {st}")
+    return ExitLaw(rho, reach, w, cov, logZ)
+
+
+@dataclass
+class Draws:
+    exit_node: np.ndarray    # [R][n] int32
+    bonus_token: np.ndarray  # [R][n] int32
+    band_exit: np.ndarray    # [R][n] bool: u1 within 1e-6 of a boundary of its bin
+    band_bonus: np.ndarray   # [R][n] bool
+
+
+def sample(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
+           exit_mass: np.ndarray, uniforms: np.ndarray, inv_temperature: float = 1.0,
+           nthreads: int = 0) -> Draws:
+    """TEV's exit-node and bonus-token draws (2610.11750 App. B, Algorithm 1)."""
+    lg = _as_input(logits, dtype)
+    if lg.ndim == 2:
+        lg = lg[None]
+    R, B, V = lg.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(R, B)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(R, B)
+    w = np.ascontiguousarray(exit_mass, dtype=np.float64).reshape(R, B)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(R, -1, 2)
+    n = u.shape[1]
+    en = np.empty((R, n), np.int32); bt = np.empty((R, n), np.int32)
+    band = np.empty((R, n, 2), np.uint8)
+    st = _load().oracle_sample(_ptr(lg), _DTYPE_CODES[dtype], _ptr(par), _ptr(tok), R, B, V,
+                               float(inv_temperature), _ptr(w), _ptr(u), n, _ptr(en), _ptr(bt),
+                               _ptr(band), int(nthreads))
+    if st != 0:
+        raise OracleError(f"oracle_sample failed with status {st}")
+    return Draws(en, bt, band[..., 0].astype(bool), band[..., 1].astype(bool))
+
+
+def residual_cdf(logits_req: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
+                 node: int, inv_temperature: float = 1.0) -> np.ndarray:
+    """Normalised residual CDF of one node's row in token order (Eq. 7)."""
+    lg = _as_input(logits_req, dtype)
+    B, V = lg.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(B)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B)
+    out = np.empty(V)
+    st = _load().oracle_residual_cdf(_ptr(lg), _DTYPE_CODES[dtype], _ptr(par), _ptr(tok), B, V,
+                                     int(node), float(inv_temperature), _ptr(out))
+    if st != 0:
+        raise OracleError(f"oracle_residual_cdf failed with status {st}")
+    return out
+
+
+def tree_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, parents: np.ndarray,
+              P: int, scale: float, rows: np.ndarray | None = None,
+              nthreads: int = 0) -> np.ndarray:
+    """Ancestor-masked tree attention (2610.00321 App. B Lemma 1, App. C).
+
+    q [R][B][Hq][D]; k, v [R][Hkv][P+B][D].  Returns [R][B][Hq][D] float64, or
+    [len(rows)][D] for the flat query indices in ``rows``.
+    """
+    qq = _as_input(q, dtype); kk = _as_input(k, dtype); vv = _as_input(v, dtype)
+    R, B, Hq, D = qq.shape
+    Hkv = kk.shape[1]
+    if kk.shape != (R, Hkv, P + B, D) or vv.shape != kk.shape:
+        raise ValueError("k/v shape must be [R][Hkv][P+B][D]")
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(R, B)
+    if rows is None:
+        out = np.empty((R, B, Hq, D))
+        rr, nr = None, 0
+    else:
+        rr = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = int(rr.shape[0])
+        out = np.empty((nr, D))
+    st = _load().oracle_tree_attn(_ptr(qq), _ptr(kk), _ptr(vv), _DTYPE_CODES[dtype], _ptr(par),
+                                  R, B, Hq, Hkv, D, int(P), float(scale), _ptr(out), _ptr(rr),
+                                  nr, int(nthreads))
+    if st != 0:
+        raise OracleError(f"oracle_tree_attn failed with status {st}")
+    return out
