@@ -1,0 +1,184 @@
+// tev_api.hip -- host side of the C ABI declared in include/tev.h: argument
+// checks, workspace sizing and kernel dispatch.  Nothing here allocates or
+// synchronises except the calls the header marks synchronous.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "tev_internal.h"
+
+using namespace tev;
+
+namespace {
+
+constexpr long long kMaxV = 1LL << 26;        // 67M tokens per row
+constexpr long long kMaxRows = 1LL << 16;      // R * B (grid.y of the vocabulary pass)
+
+bool dtype_ok(int dtype) { return dtype == TEV_F32 || dtype == TEV_BF16; }
+size_t esize(int dtype) { return dtype == TEV_BF16 ? 2 : 4; }
+
+tev_status check_exit_shape(int R, int B, int V) {
+    if (R < 1 || B < 1 || V < 1) return TEV_ERR_SHAPE;
+    if (B > TEV_MAX_NODES || V > kMaxV || (long long)R * B > kMaxRows) return TEV_ERR_SHAPE;
+    return TEV_OK;
+}
+
+bool vec_ok(const void *logits, int dtype, int V) {
+    return ((uintptr_t)logits % 16 == 0) && (((size_t)V * esize(dtype)) % 16 == 0);
+}
+
+float log2e_scale(float inv_temperature) {
+    return (float)((double)inv_temperature * 1.4426950408889634);
+}
+
+tev_status hip_status(hipError_t e) { return e == hipSuccess ? TEV_OK : TEV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *tev_status_str(int s) {
+    switch (s) {
+        case TEV_OK: return "ok";
+        case TEV_ERR_NULL: return "null pointer argument";
+        case TEV_ERR_SHAPE: return "size out of range or inconsistent";
+        case TEV_ERR_DTYPE: return "unsupported dtype";
+        case TEV_ERR_TREE: return "invalid tree (parents/tokens)";
+        case TEV_ERR_WORKSPACE: return "workspace too small";
+        case TEV_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TEV_ERR_HIP: return "HIP runtime error";
+        case TEV_ERR_VALUE: return "scalar argument not finite or not positive";
+        default: return "unknown status";
+    }
+}
+
+size_t tev_exit_law_workspace_bytes(int R, int B, int V) {
+    if (check_exit_shape(R, B, V) != TEV_OK) return 0;
+    return exit_ws_layout(R, B, V).total;
+}
+
+tev_status tev_exit_law(const void *logits, int dtype, const int32_t *parents,
+                        const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                        float *rho, float *reach, float *exit_mass, float *coverage,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!logits || !parents || !tokens || !rho || !reach || !exit_mass || !coverage || !workspace)
+        return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
+    if (workspace_bytes < exit_ws_layout(R, B, V).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_exit_law(logits, dtype, vec_ok(logits, dtype, V), parents, tokens, R,
+                                      B, V, log2e_scale(inv_temperature), rho, reach, exit_mass,
+                                      coverage, (char *)workspace, (hipStream_t)stream));
+}
+
+tev_status tev_sample(const void *logits, int dtype, const int32_t *parents,
+                      const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                      const void *workspace, size_t workspace_bytes, const float *uniforms,
+                      int n_draws, int32_t *exit_node, int32_t *bonus_token, void *stream) {
+    if (!logits || !parents || !tokens || !workspace || !uniforms || !exit_node || !bonus_token)
+        return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    if (n_draws < 1 || n_draws > 65535) return TEV_ERR_SHAPE;
+    if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
+    if (workspace_bytes < exit_ws_layout(R, B, V).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_sample(logits, dtype, vec_ok(logits, dtype, V), parents, tokens, R, B,
+                                    V, log2e_scale(inv_temperature), (const char *)workspace,
+                                    uniforms, n_draws, exit_node, bonus_token,
+                                    (hipStream_t)stream));
+}
+
+size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {
+    if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0) return 0;
+    if (D != 64 && D != 128) return 0;
+    return attn_ws_layout(R, B, Hq, Hkv, D, P).total;
+}
+
+tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
+                         const int32_t *parents, int R, int B, int Hq, int Hkv, int D, int P,
+                         float scale, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    if (!q || !k || !v || !parents || !out || !workspace) return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || P < 0) return TEV_ERR_SHAPE;
+    if (Hq % Hkv) return TEV_ERR_SHAPE;
+    if ((long long)R * Hkv > 65535 || (long long)P + B > (1LL << 30)) return TEV_ERR_SHAPE;
+    if (D != 64 && D != 128) return TEV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return TEV_ERR_VALUE;
+    if (dtype == TEV_BF16 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16))
+        return TEV_ERR_UNSUPPORTED;
+    if (workspace_bytes < attn_ws_layout(R, B, Hq, Hkv, D, P).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_tree_attn(q, k, v, dtype, parents, R, B, Hq, Hkv, D, P, scale, out,
+                                       (char *)workspace, (hipStream_t)stream));
+}
+
+tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host, int B,
+                                  int V) {
+    if (!parents_host || !tokens_host) return TEV_ERR_NULL;
+    if (B < 1 || B > TEV_MAX_NODES || V < 1) return TEV_ERR_SHAPE;
+    if (parents_host[0] != -1) return TEV_ERR_TREE;
+    // per parent: the child tokens seen so far (sibling tokens must differ)
+    for (int i = 1; i < B; i++) {
+        const int p = parents_host[i];
+        if (p < 0 || p >= i) return TEV_ERR_TREE;
+        if (tokens_host[i] < 0 || tokens_host[i] >= V) return TEV_ERR_TREE;
+        for (int j = 1; j < i; j++)
+            if (parents_host[j] == p && tokens_host[j] == tokens_host[i]) return TEV_ERR_TREE;
+    }
+    return TEV_OK;
+}
+
+tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
+                                  uint32_t *flags_host, void *stream) {
+    (void)B;
+    (void)V;
+    if (!workspace || !flags_host) return TEV_ERR_NULL;
+    if (R < 1) return TEV_ERR_SHAPE;
+    if (kind != 0 && kind != 1) return TEV_ERR_SHAPE;
+    // Both layouts place the status words first.
+    hipError_t e = hipMemcpyAsync(flags_host, workspace, sizeof(uint32_t) * (size_t)R,
+                                  hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    return hip_status(e);
+}
+
+tev_status tev_export_exit_cdf(const void *workspace, int R, int B, int V, double *cdf_host,
+                               void *stream) {
+    if (!workspace || !cdf_host) return TEV_ERR_NULL;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    const ExitWs L = exit_ws_layout(R, B, V);
+    hipError_t e = hipMemcpyAsync(cdf_host, (const char *)workspace + L.wcum,
+                                  sizeof(double) * (size_t)R * B, hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return TEV_ERR_HIP;
+    for (int r = 0; r < R; r++) {
+        const double S = cdf_host[(size_t)r * B + B - 1];
+        for (int j = 0; j < B; j++) cdf_host[(size_t)r * B + j] /= S;
+    }
+    return TEV_OK;
+}
+
+tev_status tev_export_residual_cdf(const void *logits, int dtype, const int32_t *parents,
+                                   const int32_t *tokens, int R, int B, int V,
+                                   float inv_temperature, const void *workspace,
+                                   size_t workspace_bytes, int r, int node, double *cdf,
+                                   void *stream) {
+    if (!logits || !parents || !tokens || !workspace || !cdf) return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    if (r < 0 || r >= R || node < 0 || node >= B) return TEV_ERR_SHAPE;
+    if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
+    if (workspace_bytes < exit_ws_layout(R, B, V).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_residual_cdf(logits, dtype, vec_ok(logits, dtype, V), parents, tokens,
+                                          R, B, V, log2e_scale(inv_temperature),
+                                          (const char *)workspace, r, node, cdf,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// tev_internal.h -- workspace layouts and launcher declarations shared by the
+// HIP translation units of libtev.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tev.h"
+
+namespace tev {
+
+// The vocabulary pass splits every logit row into chunks of CHUNK tokens; one
+// workgroup of VOCAB_THREADS threads reduces one (row, chunk) pair, each thread
+// holding CHUNK / VOCAB_THREADS elements in registers.
+constexpr int CHUNK = 8192;
+constexpr int VOCAB_THREADS = 256;
+constexpr int EPT = CHUNK / VOCAB_THREADS;   // 32 elements per thread
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int n_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }
+
+// Exit-law workspace, per request r, node v, chunk c (nc chunks per row):
+//   status  u32 [R]          device flag bits of the request (TEV_FLAG_*)
+//   flags   u32 [R][B][nc]   per-(row, chunk) flags from the vocabulary pass
+//   part_m  f32 [R][B][nc]   chunk offset M_c in log2 units (max logit * sL)
+//   part_r  f64 [R][B][nc]   chunk residual sum  sum_{a in c, a not child} 2^(l_a sL - M_c)
+//   part_c  f64 [R][B][nc]   chunk child sum     sum_{a in c, a child}     2^(l_a sL - M_c)
+//   row_m   f32 [R][B]       row offset M_v = max_c M_c
+//   rcum    f64 [R][B][nc]   running residual sum over chunks, units 2^(-M_v)
+//   wcum    f64 [R][B]       running exit mass over nodes in index order
+struct ExitWs {
+    size_t status, flags, part_m, part_r, part_c, row_m, rcum, wcum, total;
+};
+
+inline ExitWs exit_ws_layout(int R, int B, int V) {
+    const size_t rb = (size_t)R * B, rbc = rb * (size_t)n_chunks(V);
+    ExitWs L{};
+    size_t o = 0;
+    L.status = o; o = align_up(o + 4 * (size_t)R, 256);
+    L.flags = o;  o = align_up(o + 4 * rbc, 256);
+    L.part_m = o; o = align_up(o + 4 * rbc, 256);
+    L.part_r = o; o = align_up(o + 8 * rbc, 256);
+    L.part_c = o; o = align_up(o + 8 * rbc, 256);
+    L.row_m = o;  o = align_up(o + 4 * rb, 256);
+    L.rcum = o;   o = align_up(o + 8 * rbc, 256);
+    L.wcum = o;   o = align_up(o + 8 * rb, 256);
+    L.total = o;
+    return L;
+}
+
+// Tree-attention workspace:
+//   status  u32 [R]
+//   part_o  f32 [S][R*Hkv][G*B][D]  un-normalised split outputs (S splits)
+//   part_ml f32 [S][R*Hkv][G*B][2]  running max (log2 units) and sum
+struct AttnPlan {
+    int nqt, nw;          // query tiles (16 rows) per wave, waves per workgroup
+    int rows_per_wg;      // nw * nqt * 16
+    int row_blocks;       // ceil(G*B / rows_per_wg)
+    int splits;           // prefix splits
+    int keys_per_split;   // multiple of 32
+};
+
+struct AttnWs {
+    size_t status, part_o, part_ml, total;
+};
+
+AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P);
+
+inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P) {
+    AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P);
+    const int G = Hq / Hkv;
+    const size_t rows = (size_t)R * Hkv * G * B;
+    AttnWs L{};
+    size_t o = 0;
+    L.status = o; o = align_up(o + 4 * (size_t)R, 256);
+    const size_t S = pl.splits > 1 ? (size_t)pl.splits : 0;
+    L.part_o = o;  o = align_up(o + 4 * S * rows * D, 256);
+    L.part_ml = o; o = align_up(o + 8 * S * rows, 256);
+    L.total = o;
+    return L;
+}
+
+// ---- launchers (return hipGetLastError() of the launches) ----
+hipError_t launch_exit_law(const void *logits, int dtype, bool vec, const int32_t *parents,
+                           const int32_t *tokens, int R, int B, int V, float sL, float *rho,
+                           float *reach, float *exit_mass, float *coverage, char *ws,
+                           hipStream_t st);
+hipError_t launch_sample(const void *logits, int dtype, bool vec, const int32_t *parents,
+                         const int32_t *tokens, int R, int B, int V, float sL, const char *ws,
+                         const float *uniforms, int n_draws, int32_t *exit_node,
+                         int32_t *bonus_token, hipStream_t st);
+hipError_t launch_residual_cdf(const void *logits, int dtype, bool vec, const int32_t *parents,
+                               const int32_t *tokens, int R, int B, int V, float sL,
+                               const char *ws, int r, int node, double *cdf, hipStream_t st);
+hipError_t launch_tree_attn(const void *q, const void *k, const void *v, int dtype,
+                            const int32_t *parents, int R, int B, int Hq, int Hkv, int D, int P,
+                            float scale, float *out, char *ws, hipStream_t st);
+
+}  // namespace tev

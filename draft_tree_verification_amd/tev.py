@@ -1,0 +1,248 @@
+"""Python binding of libtev (include/tev.h): argument marshalling only.
+
+Every step of the verification path runs in the HIP kernels of libtev; this
+module only checks tensor shapes, allocates outputs and workspaces through
+torch, and passes raw device pointers and the current HIP stream to the C ABI.
+There is no CPU fallback: if libtev.so is missing or cannot be loaded, every
+call raises.
+
+Function names follow the C ABI: tev_exit_law, tev_sample, tev_tree_attn, ...
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libtev.so")
+
+TEV_F32, TEV_BF16 = 0, 1
+TEV_FLAG_NONFINITE, TEV_FLAG_TREE = 1, 2
+TEV_MAX_NODES = 256
+STATUS_NAMES = {0: "TEV_OK", 1: "TEV_ERR_NULL", 2: "TEV_ERR_SHAPE", 3: "TEV_ERR_DTYPE",
+                4: "TEV_ERR_TREE", 5: "TEV_ERR_WORKSPACE", 6: "TEV_ERR_UNSUPPORTED",
+                7: "TEV_ERR_HIP", 8: "TEV_ERR_VALUE"}
+
+EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
+            "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
+            "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
+            "tev_export_residual_cdf"]
+
+
+class TevError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtev.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.tev_exit_law_workspace_bytes.argtypes = [i, i, i]
+        L.tev_exit_law_workspace_bytes.restype = sz
+        L.tev_exit_law.argtypes = [vp, i, vp, vp, i, i, i, f, vp, vp, vp, vp, vp, sz, vp]
+        L.tev_sample.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp]
+        L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.tev_tree_attn_workspace_bytes.restype = sz
+        L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
+        L.tev_validate_tree_host.argtypes = [vp, vp, i, i]
+        L.tev_read_device_status.argtypes = [vp, i, i, i, i, vp, vp]
+        L.tev_status_str.argtypes = [i]
+        L.tev_status_str.restype = ctypes.c_char_p
+        L.tev_export_exit_cdf.argtypes = [vp, i, i, i, vp, vp]
+        L.tev_export_residual_cdf.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, i, i, vp, vp]
+        for fn in ("tev_exit_law", "tev_sample", "tev_tree_attn", "tev_validate_tree_host",
+                   "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise TevError(fn, st)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TEV_BF16
+    if t.dtype == torch.float32:
+        return TEV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev_i32(x, shape, device) -> torch.Tensor:
+    t = torch.as_tensor(x, dtype=torch.int32, device=device).reshape(shape).contiguous()
+    return t
+
+
+def _need_cuda(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ---------------------------------------------------------------- exit law
+@dataclass
+class ExitLawResult:
+    rho: torch.Tensor        # float32 [R][B]
+    reach: torch.Tensor      # float32 [R][B]
+    exit_mass: torch.Tensor  # float32 [R][B]
+    coverage: torch.Tensor   # float32 [R]
+    workspace: torch.Tensor  # uint8, private state read by tev_sample
+
+
+def tev_exit_law_workspace_bytes(R: int, B: int, V: int) -> int:
+    return int(lib().tev_exit_law_workspace_bytes(R, B, V))
+
+
+def tev_exit_law(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                 inv_temperature: float = 1.0, workspace: torch.Tensor | None = None,
+                 out: ExitLawResult | None = None) -> ExitLawResult:
+    """Exit law of every request: logits [R][B][V] (bf16 or f32) on the GPU,
+    parents/tokens int32 [R][B] on the GPU."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    _need_cuda(logits, parents, tokens)
+    R, B, V = logits.shape
+    dev = logits.device
+    L = lib()
+    need = tev_exit_law_workspace_bytes(R, B, V)
+    if out is None:
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        out = ExitLawResult(torch.empty((R, B), dtype=torch.float32, device=dev),
+                            torch.empty((R, B), dtype=torch.float32, device=dev),
+                            torch.empty((R, B), dtype=torch.float32, device=dev),
+                            torch.empty((R,), dtype=torch.float32, device=dev), workspace)
+    st = L.tev_exit_law(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
+                        float(inv_temperature), _p(out.rho), _p(out.reach), _p(out.exit_mass),
+                        _p(out.coverage), _p(out.workspace), out.workspace.numel(), _stream())
+    _check("tev_exit_law", st)
+    return out
+
+
+def tev_sample(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+               workspace: torch.Tensor, uniforms: torch.Tensor, inv_temperature: float = 1.0,
+               out: tuple[torch.Tensor, torch.Tensor] | None = None):
+    """TEV's exit-node and bonus-token draws; uniforms float32 [R][n][2]."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    _need_cuda(logits, parents, tokens, workspace, uniforms)
+    R, B, V = logits.shape
+    n = uniforms.shape[-2]
+    if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * 2:
+        raise ValueError("uniforms must be float32 [R][n][2]")
+    if out is None:
+        out = (torch.empty((R, n), dtype=torch.int32, device=logits.device),
+               torch.empty((R, n), dtype=torch.int32, device=logits.device))
+    st = lib().tev_sample(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
+                          float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
+                          n, _p(out[0]), _p(out[1]), _stream())
+    _check("tev_sample", st)
+    return out
+
+
+# ---------------------------------------------------------------- attention
+def tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P) -> int:
+    return int(lib().tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P))
+
+
+def tev_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor,
+                  P: int, scale: float | None = None, workspace: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """q [R][B][Hq][D], k/v [R][Hkv][P+B][D] (bf16 or f32) -> float32 [R][B][Hq][D]."""
+    _need_cuda(q, k, v, parents)
+    R, B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (R, Hkv, P + B, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must be [R][Hkv][P+B][D] with q's dtype")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    need = tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((R, B, Hq, D), dtype=torch.float32, device=q.device)
+    st = lib().tev_tree_attn(_p(q), _p(k), _p(v), _dtype_code(q), _p(parents), R, B, Hq, Hkv, D,
+                             int(P), float(scale), _p(out), _p(workspace), workspace.numel(),
+                             _stream())
+    _check("tev_tree_attn", st)
+    return out
+
+
+# ---------------------------------------------------------------- helpers
+def tev_validate_tree_host(parents: np.ndarray, tokens: np.ndarray, V: int) -> int:
+    p = np.ascontiguousarray(parents, dtype=np.int32)
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return int(lib().tev_validate_tree_host(p.ctypes.data_as(ctypes.c_void_p),
+                                            t.ctypes.data_as(ctypes.c_void_p), int(p.shape[0]), int(V)))
+
+
+def tev_read_device_status(workspace: torch.Tensor, kind: int, R: int, B: int = 1, V: int = 1) -> np.ndarray:
+    flags = np.zeros(R, np.uint32)
+    st = lib().tev_read_device_status(_p(workspace), kind, R, B, V,
+                                      flags.ctypes.data_as(ctypes.c_void_p), _stream())
+    _check("tev_read_device_status", st)
+    return flags
+
+
+def tev_status_str(status: int) -> str:
+    return lib().tev_status_str(int(status)).decode()
+
+
+def tev_export_exit_cdf(workspace: torch.Tensor, R: int, B: int, V: int) -> np.ndarray:
+    cdf = np.empty((R, B), np.float64)
+    st = lib().tev_export_exit_cdf(_p(workspace), R, B, V, cdf.ctypes.data_as(ctypes.c_void_p), _stream())
+    _check("tev_export_exit_cdf", st)
+    return cdf
+
+
+def tev_export_residual_cdf(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                            workspace: torch.Tensor, r: int, node: int,
+                            inv_temperature: float = 1.0) -> torch.Tensor:
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    R, B, V = logits.shape
+    cdf = torch.empty(V, dtype=torch.float64, device=logits.device)
+    st = lib().tev_export_residual_cdf(_p(logits), _dtype_code(logits), _p(parents), _p(tokens),
+                                       R, B, V, float(inv_temperature), _p(workspace),
+                                       workspace.numel(), int(r), int(node), _p(cdf), _stream())
+    _check("tev_export_residual_cdf", st)
+    return cdf
+
+
+# ---------------------------------------------------------------- tensors from host arrays
+def to_device_logits(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """float32 array or uint16 bf16 bit patterns -> device tensor of that dtype."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def to_device_i32(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)

@@ -1,0 +1,186 @@
+/*
+ * tev.h -- C ABI of the MI355X (gfx950) draft-tree verification library.
+ *
+ * The library runs the verification stage of tree speculative decoding on one
+ * GPU: one layer of ancestor-masked tree attention, the canonical exit law,
+ * and Tree Exit Verification (TEV)'s exit-node and bonus-token draws.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array pointer is a DEVICE pointer owned by the caller unless its
+ *    comment says "host".  The library never allocates, frees or retains
+ *    memory, and holds no global mutable state: calls are reentrant, and
+ *    calls on different workspaces may run concurrently.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call enqueues its kernels on `stream` and returns without
+ *    synchronising, except the calls marked "synchronous".
+ *  - Inputs are read only.  Outputs are fully overwritten, never accumulated.
+ *  - Arrays are row-major and contiguous.  R is the number of independent
+ *    requests, B the number of tree nodes per request INCLUDING the root
+ *    (node 0), V the vocabulary size.  A tree is given as `parents[r][i]`
+ *    (parents[r][0] = -1 and 0 <= parents[r][i] < i for i >= 1, i.e. any
+ *    ancestor-before-descendant order) and `tokens[r][i]`, the incoming token
+ *    of node i (0 <= tokens[r][i] < V for i >= 1; tokens[r][0] is not read).
+ *    Sibling tokens must be distinct.  1 <= B <= TEV_MAX_NODES.
+ *  - Errors a host can see (null pointers, bad sizes, unsupported dtype,
+ *    workspace too small) return a status before anything is enqueued.
+ *    Errors only the device can see (NaN or +inf logits, a row that is
+ *    entirely -inf, an invalid tree) set per-request flag bits in the
+ *    workspace; that request's float outputs become NaN and its integer
+ *    outputs -1.  -inf logits are allowed and mean probability zero.
+ *  - No C++ exception crosses this boundary.
+ *
+ * Sources (titles of the pages the operations are defined on):
+ *  [EXIT] "Where Draft Trees Lose Target Mass: Exit-Guided Speculative
+ *         Decoding" (arXiv 2610.11750): Sec. 3 Eq. 1-2, Sec. 3.1 Eq. 4,
+ *         Lemma 1 Eq. 5, Sec. 3.2 Eq. 6-7, App. B Algorithm 1.
+ *  [CAST] "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
+ *         (arXiv 2610.00321): App. B Lemma 1, App. C "Packed verification",
+ *         App. F varlen tree-attention verifier.
+ */
+#ifndef TEV_H
+#define TEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TEV_MAX_NODES 256
+
+typedef enum {
+    TEV_OK = 0,
+    TEV_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    TEV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent            */
+    TEV_ERR_DTYPE = 3,       /* dtype code unknown or unsupported for this call   */
+    TEV_ERR_TREE = 4,        /* host-side tree validation failed                  */
+    TEV_ERR_WORKSPACE = 5,   /* workspace smaller than *_workspace_bytes()        */
+    TEV_ERR_UNSUPPORTED = 6, /* e.g. head_dim not in {64, 128}                    */
+    TEV_ERR_HIP = 7,         /* a HIP runtime call or launch failed               */
+    TEV_ERR_VALUE = 8        /* a scalar argument is not finite / not positive    */
+} tev_status;
+
+typedef enum { TEV_F32 = 0, TEV_BF16 = 1 } tev_dtype;
+
+/* Per-request device flag bits (see tev_read_device_status). */
+#define TEV_FLAG_NONFINITE 1u /* NaN or +inf logit, or a row that is all -inf */
+#define TEV_FLAG_TREE 2u      /* parents/tokens violate the tree contract      */
+
+/* ------------------------------------------------------------------------
+ * Exit law ([EXIT] Eq. 1, 2, 4, 6; Algorithm 1 lines computing rho, w, P).
+ *
+ * For every request r and node v, with x_a = inv_temperature * logits[r][v][a]:
+ *   p_v(a)   = exp(x_a) / sum_b exp(x_b)                       (Eq. 1)
+ *   rho(v)   = sum_{a not a child token of v} p_v(a); 1 at a leaf (Eq. 4)
+ *   P(0) = 1, P(u) = P(parent(u)) * p_{parent(u)}(tokens[u])    (Eq. 2)
+ *   w(v)     = P(v) * rho(v)                                   (Eq. 4)
+ *   C        = sum_{u >= 1} P(u); expected block length 1 + C  (Eq. 6)
+ *
+ * logits    [R][B][V], dtype TEV_F32 or TEV_BF16 (bf16 = upper 16 bits of
+ *           an IEEE binary32).  Vector loads are used when V * element size
+ *           is a multiple of 16 bytes and `logits` is 16-byte aligned.
+ * rho, reach, exit_mass  float [R][B] outputs;  coverage float [R] output.
+ * inv_temperature must be finite and > 0 (1.0 = the target's own law).
+ * workspace must hold tev_exit_law_workspace_bytes(R, B, V) bytes; after the
+ * call it holds the fp64 exit law and per-chunk row statistics that
+ * tev_sample reads.  Its contents are private.
+ * Each row of logits is read exactly once.
+ * ------------------------------------------------------------------------ */
+size_t tev_exit_law_workspace_bytes(int R, int B, int V);
+
+tev_status tev_exit_law(const void *logits, int dtype, const int32_t *parents,
+                        const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                        float *rho, float *reach, float *exit_mass, float *coverage,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * TEV draws ([EXIT] App. B, Algorithm 1: "Draw V ~ Categorical(w)" and
+ * "Draw Y ~ p_V if V is a leaf, otherwise p_V^res"; residual law Eq. 7).
+ *
+ * uniforms  float [R][n_draws][2]: (u1, u2) in [0, 1), the caller's control
+ *           randomness; u1 drives the exit draw and u2 the bonus draw.
+ * exit_node, bonus_token  int32 [R][n_draws] outputs.
+ * Exit node: the smallest j with u1 * S < W_j, W_j = sum_{i <= j} w(i) in
+ * node-index order, S = W_{B-1} (fp64).  Bonus token: the smallest token a
+ * with u2 * T < R_a, R_a the running sum in token-id order of node V's
+ * residual p_V(a) * [a is not a child token of V], T its total.
+ * `workspace` must be the one filled by tev_exit_law for the same logits,
+ * tree, sizes and inv_temperature, earlier on the same stream (or ordered
+ * before this call).  tev_sample does not modify it.
+ * ------------------------------------------------------------------------ */
+tev_status tev_sample(const void *logits, int dtype, const int32_t *parents,
+                      const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                      const void *workspace, size_t workspace_bytes,
+                      const float *uniforms, int n_draws,
+                      int32_t *exit_node, int32_t *bonus_token, void *stream);
+
+/* ------------------------------------------------------------------------
+ * One layer of ancestor-masked tree attention ([CAST] App. B Lemma 1 and
+ * App. C "Packed verification": every packed node attends to all P cached
+ * prefix entries and to the entries of its own root path, itself included).
+ *
+ * q     [R][B][Hq][D];  k, v  [R][Hkv][P + B][D]: cache rows 0..P-1 are the
+ *       prefix, row P + i holds tree node i (row P is the root); rotary
+ *       phases are already applied by the caller.
+ * out   float [R][B][Hq][D]:
+ *       out[r,i,h,:] = sum_j softmax_j(scale * <q[r,i,h,:], k[r,g,j,:]>) v[r,g,j,:]
+ *       over j in {0..P-1} U {P + a : a on the root path of i}, with kv head
+ *       g = h / (Hq / Hkv).
+ * dtype TEV_BF16 (MFMA kernels, fp32 accumulation) or TEV_F32 (vector-ALU
+ * kernel).  D must be 64 or 128; Hq % Hkv == 0; P >= 0; scale finite.
+ * parents [R][B] as above (tokens are not needed).
+ * workspace must hold tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P) bytes
+ * (partial results of split-prefix launches and per-request status).
+ * ------------------------------------------------------------------------ */
+size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P);
+
+tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
+                         const int32_t *parents, int R, int B, int Hq, int Hkv, int D, int P,
+                         float scale, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host-side helpers.
+ * ------------------------------------------------------------------------ */
+
+/* Validates one tree held in HOST memory (parents_host, tokens_host [B])
+ * against the contract above.  Touches no GPU.  TEV_OK or TEV_ERR_TREE. */
+tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host,
+                                  int B, int V);
+
+/* Copies the R per-request flag words (TEV_FLAG_*) of an exit-law or
+ * tree-attention workspace into flags_host [R].  `kind` is 0 for an exit-law
+ * workspace (sizes R, B, V) and 1 for a tree-attention workspace (B, Hq, Hkv,
+ * D, P ignored for the lookup but R must match).  Synchronous: waits for
+ * `stream`. */
+tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
+                                  uint32_t *flags_host, void *stream);
+
+/* Static description of a status code. */
+const char *tev_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Verification exports.  These expose the CDFs the sampler searches, so that
+ * a test can bound their deviation from an independent computation.
+ * ------------------------------------------------------------------------ */
+
+/* Normalised exit CDF W_j / S of every request, fp64, into cdf_host [R][B]
+ * (HOST).  Synchronous. */
+tev_status tev_export_exit_cdf(const void *workspace, int R, int B, int V, double *cdf_host,
+                               void *stream);
+
+/* Normalised residual CDF of node `node` of request `r`, in token order, as
+ * the sampler evaluates it (chunk running sums plus the in-chunk scan), into
+ * the DEVICE array cdf [V] (fp64).  Same logits/tree/workspace as tev_sample. */
+tev_status tev_export_residual_cdf(const void *logits, int dtype, const int32_t *parents,
+                                   const int32_t *tokens, int R, int B, int V,
+                                   float inv_temperature, const void *workspace,
+                                   size_t workspace_bytes, int r, int node, double *cdf,
+                                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TEV_H */

@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/tev.h declares, and rejects bad arguments with the documented status
+before touching a GPU.  CPU only (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from draft_tree_verification_amd import tev
+from draft_tree_verification_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "tev.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tev_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tev.lib()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tev.EXPORTED)
+
+
+def test_status_strings():
+    for code in range(9):
+        assert tev.tev_status_str(code) != "unknown status"
+    assert tev.tev_status_str(99) == "unknown status"
+
+
+def test_host_tree_validation():
+    rng = np.random.default_rng(0)
+    p, t = W.random_tree(40, 100, rng)
+    assert tev.tev_validate_tree_host(p, t, 100) == 0
+    bad = p.copy(); bad[0] = 0
+    assert tev.tev_validate_tree_host(bad, t, 100) == 4
+    bad = p.copy(); bad[5] = 7
+    assert tev.tev_validate_tree_host(bad, t, 100) == 4
+    bad_t = t.copy(); bad_t[3] = 100
+    assert tev.tev_validate_tree_host(p, bad_t, 100) == 4
+    # duplicate sibling tokens
+    p2 = np.array([-1, 0, 0], np.int32); t2 = np.array([0, 5, 5], np.int32)
+    assert tev.tev_validate_tree_host(p2, t2, 10) == 4
+    assert tev.tev_validate_tree_host(np.zeros(300, np.int32), np.zeros(300, np.int32), 10) == 2
+
+
+def test_argument_errors_return_before_any_launch():
+    L = tev.lib()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks
+    null = None
+    s = ctypes.c_void_p(0)
+    # null pointers
+    assert L.tev_exit_law(null, 1, fake, fake, 1, 4, 10, 1.0, fake, fake, fake, fake, fake, 1 << 20, s) == 1
+    # bad sizes
+    assert L.tev_exit_law(fake, 1, fake, fake, 1, 0, 10, 1.0, fake, fake, fake, fake, fake, 1 << 20, s) == 2
+    assert L.tev_exit_law(fake, 1, fake, fake, 1, 257, 10, 1.0, fake, fake, fake, fake, fake, 1 << 20, s) == 2
+    # dtype
+    assert L.tev_exit_law(fake, 7, fake, fake, 1, 4, 10, 1.0, fake, fake, fake, fake, fake, 1 << 20, s) == 3
+    # temperature
+    assert L.tev_exit_law(fake, 1, fake, fake, 1, 4, 10, 0.0, fake, fake, fake, fake, fake, 1 << 20, s) == 8
+    assert L.tev_exit_law(fake, 1, fake, fake, 1, 4, 10, float("nan"), fake, fake, fake, fake, fake, 1 << 20, s) == 8
+    # workspace too small
+    need = L.tev_exit_law_workspace_bytes(1, 4, 10)
+    assert need > 0
+    assert L.tev_exit_law(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, fake, fake, fake, fake, need - 1, s) == 5
+    # sampler
+    assert L.tev_sample(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, need, fake, 0, fake, fake, s) == 2
+    assert L.tev_sample(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, need - 1, fake, 5, fake, fake, s) == 5
+    assert L.tev_sample(fake, 1, fake, fake, 1, 4, 10, 1.0, null, need, fake, 5, fake, fake, s) == 1
+    # attention
+    need_a = L.tev_tree_attn_workspace_bytes(1, 4, 8, 2, 128, 100)
+    assert need_a > 0
+    assert L.tev_tree_attn_workspace_bytes(1, 4, 8, 3, 128, 100) == 0
+    assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 3, 128, 100, 0.1, fake, fake, need_a, s) == 2
+    assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 2, 96, 100, 0.1, fake, fake, need_a, s) == 6
+    assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a - 1, s) == 5
+    assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 2, 128, 100, float("inf"), fake, fake, need_a, s) == 8
+    assert L.tev_tree_attn(fake, fake, fake, 1, null, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 1
+    assert L.tev_tree_attn(fake, fake, fake, 5, fake, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 3
+    # exports
+    assert L.tev_export_residual_cdf(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, need, 1, 0, fake, s) == 2
+    assert L.tev_read_device_status(null, 0, 1, 4, 10, fake, s) == 1
+
+
+def test_workspace_sizes_grow_with_problem():
+    L = tev.lib()
+    a = L.tev_exit_law_workspace_bytes(1, 64, 151936)
+    b = L.tev_exit_law_workspace_bytes(32, 64, 151936)
+    assert 0 < a < b
+    assert L.tev_exit_law_workspace_bytes(1, 64, 0) == 0

@@ -1,0 +1,74 @@
+"""GPU parity of tev_tree_attn against the CPU oracle (through the C ABI).
+
+Small cases compare every row; the named workloads run at full size, in the
+launch configuration the benchmark times, and compare sampled rows (every head
+of a few nodes, plus random rows) that the oracle computes one by one."""
+import numpy as np
+import pytest
+
+from draft_tree_verification_amd import tev
+from draft_tree_verification_amd import workloads as W
+from tests import gpu_parity as GP
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    dict(name="bf16_d128_ragged", R=2, B=37, Hq=8, Hkv=2, D=128, P=300, tree="random"),
+    dict(name="bf16_d64", R=1, B=50, Hq=6, Hkv=3, D=64, P=517, tree="random"),
+    dict(name="bf16_g1", R=1, B=33, Hq=2, Hkv=2, D=128, P=96, tree="random"),
+    dict(name="bf16_no_prefix", R=1, B=40, Hq=4, Hkv=1, D=128, P=0, tree="random"),
+    dict(name="bf16_root_only", R=3, B=1, Hq=4, Hkv=2, D=128, P=200, tree="random"),
+    dict(name="bf16_chain_256", R=1, B=256, Hq=4, Hkv=2, D=128, P=64, tree="chain"),
+    dict(name="bf16_star_256", R=1, B=256, Hq=2, Hkv=1, D=128, P=1000, tree="star"),
+    dict(name="bf16_split_prefix", R=1, B=64, Hq=32, Hkv=8, D=128, P=2048, tree="best_first"),
+    dict(name="f32_d64", R=2, B=16, Hq=4, Hkv=4, D=64, P=128, tree="random", dtype="f32"),
+    dict(name="f32_d128_gqa", R=1, B=23, Hq=6, Hkv=2, D=128, P=77, tree="random", dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c["name"] for c in SMALL])
+def test_small_cases(case):
+    c = dict(case)
+    name = c.pop("name")
+    dtype = c.pop("dtype", "bf16")
+    GP.log(f"[attn] {name} {c} {dtype}")
+    wl = W.make_custom(name, V=300, dtype=dtype, n_uniform=1, **c)
+    err = GP.check_attn(wl)
+    GP.log(f"[attn] {name} ok max row error {err:.3e}")
+
+
+def _sample_rows(wl, n_random=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, wl.R * wl.B * wl.Hq, size=n_random).tolist())
+    # every head of the root, the deepest node and a middle node of request 0 and R-1
+    d = W.depths_of(wl.parents[0])
+    for r in {0, wl.R - 1}:
+        for i in {0, int(np.argmax(d)), wl.B // 2, wl.B - 1}:
+            for h in range(wl.Hq):
+                rows.add((r * wl.B + i) * wl.Hq + h)
+    return np.array(sorted(rows), np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_4b", "qwen3_8b_wide", "mixture"])
+def test_named_workloads(name):
+    GP.log(f"[attn] workload {name}")
+    wl = W.make_config(name, n_uniform=1)
+    rows = None if name == "tiny" else _sample_rows(wl)
+    err = GP.check_attn(wl, rows=rows)
+    GP.log(f"[attn] {name} ok max row error {err:.3e}")
+
+
+def test_batched_workload():
+    GP.log("[attn] workload batched (32 requests, P=32768)")
+    wl = W.make_config("batched", n_uniform=1)
+    err = GP.check_attn(wl, rows=_sample_rows(wl, n_random=64))
+    GP.log(f"[attn] batched ok max row error {err:.3e}")
+
+
+def test_invalid_tree_is_flagged():
+    wl = W.make_custom("bad", R=2, B=20, V=100, Hq=4, Hkv=2, D=128, P=64, dtype="bf16", n_uniform=1)
+    wl.parents[1, 7] = 12
+    out, flags = GP.run_attn(wl)
+    assert flags[1] & tev.TEV_FLAG_TREE and flags[0] == 0
+    assert np.all(np.isnan(out[1]))
+    assert np.all(np.isfinite(out[0]))
