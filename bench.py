@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of one verification round on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+ancestor-masked tree attention for one layer (tev_tree_attn), the exit law
+(tev_exit_law) and TEV's exit-node and bonus-token draws with one uniform pair
+per request (tev_sample).  The default workload is the Qwen3-4B-shaped round:
+1 request, B = 64 tree nodes (root included), V = 151936 bf16 logits, 32/8
+heads of dim 128 over a 4096-token KV prefix.
+
+Timing: each step's three calls are captured in a HIP graph per input copy;
+the copies form a ring larger than the 256 MB Infinity Cache, so every step
+reads its inputs from HBM.  The timed region is bracketed by a device
+synchronisation and HIP events on the stream the kernels run on.  Per-call
+durations come from HIP events around graph replays of each call alone.
+
+The CPU baseline is the fp64 oracle timed on this host's cores on whole
+rounds of the same workload (bounded to about 10 s of CPU work).
+
+Prints one JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "verified tree nodes/sec (tree-attn + exit-law + TEV) at B=64,V=152k; % HBM peak"
+CSRC = os.path.join(ROOT, "draft_tree_verification_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl):
+    """Bytes and FLOPs the method must move / compute per round (the dense
+    work of masked sibling pairs is not counted)."""
+    import numpy as np
+    from draft_tree_verification_amd import workloads as W
+    e = 2 if wl.dtype == "bf16" else 4
+    kv = 2 * wl.R * wl.Hkv * (wl.P + wl.B) * wl.D * e
+    q = wl.R * wl.B * wl.Hq * wl.D * e
+    out = wl.R * wl.B * wl.Hq * wl.D * 4
+    flops = 0
+    for r in range(wl.R):
+        d = W.depths_of(wl.parents[r])
+        flops += 4 * wl.Hq * wl.D * int(np.sum(wl.P + d + 1))
+    logits = wl.R * wl.B * wl.V * e
+    return {"attn_bytes": kv + q + out, "attn_flops": flops, "exit_law_bytes": logits,
+            "sample_bytes": wl.R * min(wl.V, 8192) * e}
+
+
+def cpu_baseline(wl, budget_s: float = 10.0):
+    """The oracle as it stands, whole rounds of the same workload."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads(0)
+    u1 = np.ascontiguousarray(wl.uniforms[:, :1, :])
+    rounds, t0 = 0, time.perf_counter()
+    while True:
+        oracle.tree_attn(wl.q, wl.k, wl.v, wl.dtype, wl.parents, wl.P, wl.scale)
+        el = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature)
+        oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, el.exit_mass, u1, wl.inv_temperature)
+        rounds += 1
+        el_t = time.perf_counter() - t0
+        if el_t >= budget_s or rounds >= 50:
+            break
+    nodes = rounds * wl.R * wl.B
+    return {"value": nodes / el_t, "unit": "nodes/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rounds} whole round(s) of the {wl.name} workload (attention + exit law "
+                      f"+ one draw per request), {el_t:.1f} s, fp64, {threads} OpenMP threads"}
+
+
+def load_traffic(config: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3_4b")
+    ap.add_argument("--ring-bytes", type=float, default=1.2e9,
+                    help="total size of the ring of input copies (defeats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--call-iters", type=int, default=100)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verification stage "
+              "runs on a single device and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from draft_tree_verification_amd import tev
+    from draft_tree_verification_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    wl = W.make_config(args.config, n_uniform=1)
+    log(f"[bench] workload {wl.name}: {wl.meta['description']} (generated in "
+        f"{time.perf_counter() - t_gen:.1f} s)")
+    R, B, V = wl.R, wl.B, wl.V
+
+    def to_dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+    base = dict(lg=to_dev(wl.logits), q=to_dev(wl.q), k=to_dev(wl.k), v=to_dev(wl.v),
+                par=tev.to_device_i32(wl.parents), tok=tev.to_device_i32(wl.tokens),
+                uni=torch.from_numpy(np.ascontiguousarray(wl.uniforms[:, :1, :])).cuda())
+    slot_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    ring = max(1, min(64, int(np.ceil(args.ring_bytes / slot_bytes))))
+    slots = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(ring - 1)]
+    log(f"[bench] {slot_bytes / 1e6:.1f} MB of inputs per round, ring of {ring} copies "
+        f"({ring * slot_bytes / 1e9:.2f} GB)")
+
+    ws_e = torch.empty(tev.tev_exit_law_workspace_bytes(R, B, V), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, tev.tev_tree_attn_workspace_bytes(R, B, wl.Hq, wl.Hkv, wl.D, wl.P)),
+                       dtype=torch.uint8, device="cuda")
+    out_attn = torch.empty((R, B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+    el_out = tev.ExitLawResult(*[torch.empty((R, B), dtype=torch.float32, device="cuda") for _ in range(3)],
+                               torch.empty((R,), dtype=torch.float32, device="cuda"), ws_e)
+    draws = (torch.empty((R, 1), dtype=torch.int32, device="cuda"),
+             torch.empty((R, 1), dtype=torch.int32, device="cuda"))
+
+    def call_attn(s):
+        tev.tev_tree_attn(s["q"], s["k"], s["v"], s["par"], wl.P, wl.scale, workspace=ws_a, out=out_attn)
+
+    def call_exit(s):
+        tev.tev_exit_law(s["lg"], s["par"], s["tok"], wl.inv_temperature, out=el_out)
+
+    def call_sample(s):
+        tev.tev_sample(s["lg"], s["par"], s["tok"], ws_e, s["uni"], wl.inv_temperature, out=draws)
+
+    def step(s):
+        call_attn(s)
+        call_exit(s)
+        call_sample(s)
+
+    # eager check of one round before capture
+    step(slots[0])
+    torch.cuda.synchronize()
+    cov = float(el_out.coverage[0])
+    assert np.isfinite(cov), "exit law returned a non-finite coverage"
+    log(f"[bench] eager round ok: coverage {cov:.4f}, exit node {int(draws[0][0, 0])}, "
+        f"bonus {int(draws[1][0, 0])}")
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        graphs = []
+        with torch.cuda.stream(stream):
+            for s in slots:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn(s)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    g_step = capture(step)
+    log(f"[bench] captured {len(g_step)} round graphs")
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            g_step[i % ring].replay()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for i in range(args.steps):
+            g_step[i % ring].replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = R * B / (ms_per_step * 1e-3)
+    log(f"[bench] {ms_per_step * 1e3:.2f} us per round -> {value / 1e6:.3f} M nodes/s")
+
+    # per-call durations (graph replays of one call, same ring, same stream)
+    per_call = {}
+    for name, fn in (("tev_tree_attn", call_attn), ("tev_exit_law", call_exit), ("tev_sample", call_sample)):
+        gs = capture(fn)
+        with torch.cuda.stream(stream):
+            for i in range(10):
+                gs[i % ring].replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for i in range(args.call_iters):
+                gs[i % ring].replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_call[name] = a.elapsed_time(b) / args.call_iters * 1e3   # us
+        del gs
+    log(f"[bench] per call (us): " + ", ".join(f"{k} {v:.2f}" for k, v in per_call.items()))
+
+    work = algorithmic_work(wl)
+    attn_us, exit_us = per_call["tev_tree_attn"], per_call["tev_exit_law"]
+    attn_gbs = work["attn_bytes"] / (attn_us * 1e-6) / 1e9
+    attn_tfs = work["attn_flops"] / (attn_us * 1e-6) / 1e12
+    exit_gbs = work["exit_law_bytes"] / (exit_us * 1e-6) / 1e9
+    attn_hbm_bound = work["attn_bytes"] / HBM_PEAK_GBS > work["attn_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e3
+    kernels = {
+        "tev_tree_attn": {"us": round(attn_us, 3), "bytes": work["attn_bytes"], "flops": work["attn_flops"],
+                          "GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tfs, 2),
+                          "bound": "hbm" if attn_hbm_bound else "mfma",
+                          "frac": round(attn_gbs / HBM_PEAK_GBS if attn_hbm_bound else attn_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "tev_exit_law": {"us": round(exit_us, 3), "bytes": work["exit_law_bytes"], "GB/s": round(exit_gbs, 1),
+                         "bound": "hbm", "frac": round(exit_gbs / HBM_PEAK_GBS, 4)},
+        "tev_sample": {"us": round(per_call["tev_sample"], 3)},
+    }
+    dominant = "tev_tree_attn" if attn_us >= exit_us else "tev_exit_law"
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(wl.name, src_hash)
+    if dominant == "tev_tree_attn":
+        if attn_hbm_bound:
+            roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(attn_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(exit_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(exit_gbs / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dominant
+    roof["traffic"] = (traffic or {}).get(dominant, {}).get("bytes_per_launch") if traffic else None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.1f} nodes/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded; shapes of the pages' Qwen3 workloads)",
+        "config": {"workload": wl.name, "requests": R, "nodes_per_request": B, "vocab": V,
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D, "kv_prefix": wl.P,
+                   "draws_per_request": 1, "ring_copies": ring, "graph": True},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "kernel_source_hash": src_hash,
+        "inputs": wl.digests(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

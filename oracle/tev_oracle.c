@@ -100,6 +100,9 @@ static void tree_depths(const int32_t *parents, int B, int *depth) {
 
 /* Row softmax pieces of Eq. 1: x_a = s * l_a, m = max_a x_a,
  * Z = sum_a exp(x_a - m), so that p(a) = exp(x_a - m) / Z.
+ * Sums over the vocabulary are accumulated in long double (x87 extended
+ * precision) so that the identities checked below hold to 1e-12 even for
+ * V ~ 1.5e5 terms.
  * Returns 0, or 5 if the row holds NaN or +inf or is entirely -inf. */
 static int row_softmax_parts(const void *logits, int dtype, size_t row_off, int V, double s,
                              double *m_out, double *Z_out) {
@@ -110,10 +113,10 @@ static int row_softmax_parts(const void *logits, int dtype, size_t row_off, int 
         if (x > m) m = x;
     }
     if (m == -INFINITY) return 5;
-    double Z = 0.0;
-    for (int a = 0; a < V; a++) Z += exp(s * widen(logits, dtype, row_off + (size_t)a) - m);
+    long double Z = 0.0L;
+    for (int a = 0; a < V; a++) Z += (long double)exp(s * widen(logits, dtype, row_off + (size_t)a) - m);
     *m_out = m;
-    *Z_out = Z;
+    *Z_out = (double)Z;
     return 0;
 }
 
@@ -162,7 +165,7 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
         /* A(v): tokens of v's children. */
         unsigned char *in_A = (unsigned char *)calloc((size_t)V, 1);
         int n_children = 0;
-        double child_sum = 0.0;
+        long double child_sum = 0.0L;
         for (int u = 1; u < B; u++)
             if (par[u] == v) {
                 in_A[tok[u]] = 1;
@@ -173,10 +176,11 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
         if (n_children == 0) {
             res = 1.0; /* a leaf exits with certainty (Sec. 3.1) */
         } else {
+            long double acc = 0.0L;
             for (int a = 0; a < V; a++)
-                if (!in_A[a]) res += exp(inv_temperature * widen(logits, dtype, row + (size_t)a) - m[rv]);
-            res /= Z[rv];
-            if (fabs(res - (1.0 - child_sum)) > 1e-12) {
+                if (!in_A[a]) acc += (long double)exp(inv_temperature * widen(logits, dtype, row + (size_t)a) - m[rv]);
+            res = (double)(acc / (long double)Z[rv]);
+            if (fabs(res - (double)(1.0L - child_sum)) > 1e-12) {
 #pragma omp critical
                 status = 2;
             }
@@ -199,7 +203,7 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
             double p_child = exp(inv_temperature * widen(logits, dtype, prow * V + (size_t)tok[i]) - m[prow]) / Z[prow];
             P[i] = P[par[i]] * p_child;
         }
-        double C = 0.0, wsum = 0.0, wdepth = 0.0;
+        long double C = 0.0L, wsum = 0.0L, wdepth = 0.0L;
         int *depth = (int *)malloc(sizeof(int) * (size_t)B);
         tree_depths(par, B, depth);
         for (int v = 0; v < B; v++) {
@@ -210,9 +214,9 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
             if (v >= 1) C += P[v];
         }
         free(depth);
-        coverage[r] = C;
-        if (fabs(wsum - 1.0) > 1e-12) status = 2;
-        if (fabs(C - wdepth) > 1e-12 * (C > 1.0 ? C : 1.0)) status = 2;
+        coverage[r] = (double)C;
+        if (fabsl(wsum - 1.0L) > 1e-12L) status = 2;
+        if (fabsl(C - wdepth) > 1e-12L * (C > 1.0L ? C : 1.0L)) status = 2;
     }
     free(m);
     free(Z);
@@ -234,15 +238,15 @@ int oracle_residual_cdf(const void *logits, int dtype, const int32_t *parents, c
     if (!in_A) return 4;
     for (int u = 1; u < B; u++)
         if (parents[u] == node) in_A[tokens[u]] = 1;
-    double run = 0.0;
+    long double run = 0.0L;
     for (int a = 0; a < V; a++) {
         double ra = in_A[a] ? 0.0 : exp(inv_temperature * widen(logits, dtype, (size_t)node * V + a) - m) / Z;
-        run += ra;
-        cdf[a] = run;
+        run += (long double)ra;
+        cdf[a] = (double)run;
     }
     free(in_A);
-    if (!(run > 0.0)) return 5;
-    for (int a = 0; a < V; a++) cdf[a] /= run;
+    if (!(run > 0.0L)) return 5;
+    for (int a = 0; a < V; a++) cdf[a] = (double)((long double)cdf[a] / run);
     return 0;
 }
 
