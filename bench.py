@@ -147,8 +147,8 @@ def main():
     log(f"[bench] {slot_bytes / 1e6:.1f} MB of inputs per round, ring of {ring} copies "
         f"({ring * slot_bytes / 1e9:.2f} GB)")
 
-    ws_e = torch.empty(tev.tev_exit_law_workspace_bytes(R, B, V), dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(max(1, tev.tev_tree_attn_workspace_bytes(R, B, wl.Hq, wl.Hkv, wl.D, wl.P)),
+    ws_e = torch.zeros(tev.tev_exit_law_workspace_bytes(R, B, V), dtype=torch.uint8, device="cuda")
+    ws_a = torch.zeros(max(1, tev.tev_tree_attn_workspace_bytes(R, B, wl.Hq, wl.Hkv, wl.D, wl.P)),
                        dtype=torch.uint8, device="cuda")
     out_attn = torch.empty((R, B, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
     el_out = tev.ExitLawResult(*[torch.empty((R, B), dtype=torch.float32, device="cuda") for _ in range(3)],

@@ -11,11 +11,13 @@
 namespace tev {
 
 // The vocabulary pass splits every logit row into chunks of CHUNK tokens; one
-// workgroup of VOCAB_THREADS threads reduces one (row, chunk) pair, each thread
-// holding CHUNK / VOCAB_THREADS elements in registers.
-constexpr int CHUNK = 8192;
+// wavefront (64 lanes) reduces one (row, chunk) pair on its own, each lane
+// holding EPT = 64 elements in registers.  A workgroup of VOCAB_THREADS
+// threads runs four such independent waves on consecutive chunks of a row.
+constexpr int CHUNK = 4096;
 constexpr int VOCAB_THREADS = 256;
-constexpr int EPT = CHUNK / VOCAB_THREADS;   // 32 elements per thread
+constexpr int WAVES_PER_WG = VOCAB_THREADS / 64;
+constexpr int EPT = CHUNK / 64;   // 64 elements per lane
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int n_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }

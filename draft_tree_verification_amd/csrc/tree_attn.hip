@@ -28,7 +28,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "tev_internal.h"
+#include "wave_ops.h"
 
 namespace tev {
 namespace {
@@ -158,30 +162,46 @@ __device__ __forceinline__ uint32_t max_mag8(const uint4 &x) {
     return m;
 }
 
+constexpr int PD = 4;   // K/V blocks in flight per workgroup (register prefetch depth)
+
+// Grid: a 1-D list of n_wg workgroup tasks (row block, prefix split, request *
+// kv head), row block fastest.  Hardware dispatches workgroup i to XCD i % 8,
+// so task L = (i % 8) * ceil(n_wg / 8) + i / 8 puts consecutive tasks -- the
+// row blocks that stream the same K/V -- on the same XCD and its L2.
 template <int D, int NQT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_mfma(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ parents, int B, int Hq, int Hkv,
-    int P, float c_log2, int splits, int keys_per_split, float *__restrict__ out,
-    float *__restrict__ part_o, float *__restrict__ part_ml, unsigned *__restrict__ status) {
+    int P, float c_log2, int row_blocks, int splits, int keys_per_split, int n_wg,
+    float *__restrict__ out, float *__restrict__ part_o, float *__restrict__ part_ml,
+    unsigned *__restrict__ status) {
     constexpr int NT = NW * 64;
     constexpr int DS = D / 32;          // k-steps of the score product
     constexpr int DT = D / 16;          // 16-row tiles of O^T
     constexpr int KROW = D + 8;         // K row stride in LDS (bf16 elements)
-    constexpr int VROW = KB + 4;        // V^T row stride in LDS (bf16 elements)
+    constexpr int VROW = KB + 4;        // V^T row stride in LDS (fp16 elements)
     constexpr int WR = NW * NQT * 16;   // query rows per workgroup
     constexpr int K_ITEMS = KB * D / 8;         // 16-byte chunks of a K block
     constexpr int V_ITEMS = (KB / 2) * (D / 8); // (key pair, 8-column) items of a V block
     constexpr int NKI = (K_ITEMS + NT - 1) / NT;
     constexpr int NVI = (V_ITEMS + NT - 1) / NT;
 
+    const int per_xcd = (n_wg + 7) / 8;
+    const int task = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (task >= n_wg) return;
+    const int rb = task % row_blocks;
+    const int sp = (task / row_blocks) % splits;
+    const int rg = task / (row_blocks * splits);
+
     const int G = Hq / Hkv;
     const int rows_total = G * B;
-    const int rb = blockIdx.x, sp = blockIdx.y, rg = blockIdx.z;
     const int r = rg / Hkv, g = rg - r * Hkv;
     const int tid = threadIdx.x;
+    __builtin_assume(tid < NT);
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
+    constexpr bool K_FULL = (K_ITEMS % NT) == 0;   // every thread owns NKI K chunks
+    constexpr bool V_FULL = (V_ITEMS % NT) == 0;
 
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KB * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * VROW];
@@ -195,6 +215,84 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
     const int kbeg = sp * keys_per_split;
     const int kend = last ? P + B : kbeg + keys_per_split;
     const int nkv = P + B;
+    const uint16_t *kbase = k + ((size_t)r * Hkv + g) * (size_t)nkv * D;
+    const uint16_t *vbase = v + ((size_t)r * Hkv + g) * (size_t)nkv * D;
+    const int nblocks = (kend - kbeg + KB - 1) / KB;
+
+    // PD register stages, one named array pair per stage
+    uint4 kreg0[NKI], kreg1[NKI], kreg2[NKI], kreg3[NKI];
+    uint4 vreg0[NVI][2], vreg1[NVI][2], vreg2[NVI][2], vreg3[NVI][2];
+    auto gload = [=](uint4 (&kr)[NKI], uint4 (&vr)[NVI][2], int kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NKI; n++) {
+            const int item = tid + n * NT;
+            if (K_FULL || item < K_ITEMS) {
+                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
+                const int kk = min(kb + key, nkv - 1);
+                kr[n] = *reinterpret_cast<const uint4 *>(kbase + (size_t)kk * D + d0);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVI; n++) {
+            const int item = tid + n * NT;
+            if (V_FULL || item < V_ITEMS) {
+                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
+                const int k0 = min(kb + 2 * kp, nkv - 1), k1 = min(kb + 2 * kp + 1, nkv - 1);
+                vr[n][0] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k0 * D + d0);
+                vr[n][1] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k1 * D + d0);
+            } else {
+                vr[n][0] = uint4{0u, 0u, 0u, 0u};
+                vr[n][1] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // Largest |V| of the block held in register slot sl, per wave, into s_wmax[buf].
+    auto publish_vmax = [=](const uint4 (&vr)[NVI][2], uint32_t *wmax) __attribute__((always_inline)) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int n = 0; n < NVI; n++) m = max(m, max(max_mag8(vr[n][0]), max_mag8(vr[n][1])));
+        m = (uint32_t)wave::max_i32((int)m);
+        if (lane == 0) wmax[wave] = m;
+    };
+    // K as is; V transposed and converted to fp16 times 2^-vs, with vs chosen
+    // from the block's largest |V| so that the scaled values stay below 2^15.
+    auto lstore = [=](const uint4 (&kr)[NKI], const uint4 (&vr)[NVI][2], uint16_t *sk, uint16_t *svt,
+                      const uint32_t *wmax, int *vs_out) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < NKI; n++) {
+            const int item = tid + n * NT;
+            if (K_FULL || item < K_ITEMS) {
+                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
+                *reinterpret_cast<uint4 *>(&sk[key * KROW + d0]) = kr[n];
+            }
+        }
+        uint32_t mb = 0;
+#pragma unroll
+        for (int w = 0; w < NW; w++) mb = max(mb, wmax[w]);
+        const int ebits = (int)(mb >> 7);                       // bf16 biased exponent
+        const int vs = mb == 0 ? 0 : min(max(ebits - 141, -100), 15);
+        const float vscale = __builtin_ldexpf(1.0f, -vs);
+        if (tid == 0) *vs_out = vs;
+#pragma unroll
+        for (int n = 0; n < NVI; n++) {
+            const int item = tid + n * NT;
+            if (V_FULL || item < V_ITEMS) {
+                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const uint32_t w = bf16_to_f16_scaled(half_of(vr[n][0], e), vscale) |
+                                       (bf16_to_f16_scaled(half_of(vr[n][1], e), vscale) << 16);
+                    *reinterpret_cast<uint32_t *>(&svt[(d0 + e) * VROW + 2 * kp]) = w;
+                }
+            }
+        }
+    };
+
+    // Prefetch the first PD blocks before anything else.
+    if (0 < nblocks) gload(kreg0, vreg0, kbeg);
+    if (1 < nblocks) gload(kreg1, vreg1, kbeg + KB);
+    if (2 < nblocks) gload(kreg2, vreg2, kbeg + 2 * KB);
+    if (3 < nblocks) gload(kreg3, vreg3, kbeg + 3 * KB);
 
     bool tree_ok = true;
     if (last) {
@@ -207,7 +305,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
             }
         }
         if (rb == 0 && g == 0 && tid == 0) status[r] = tree_ok ? 0u : TEV_FLAG_TREE;
-        __syncthreads();
     }
 
     // This lane's query column in each of its NQT tiles, and its Q^T operands.
@@ -226,77 +323,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
             qop[t][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + ds * 32 + grp * 8));
     }
 
-    const uint16_t *kbase = k + ((size_t)r * Hkv + g) * (size_t)nkv * D;
-    const uint16_t *vbase = v + ((size_t)r * Hkv + g) * (size_t)nkv * D;
-
-    uint4 kreg[NKI];
-    uint4 vreg[NVI][2];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int n = 0; n < NKI; n++) {
-            const int item = tid + n * NT;
-            if (item < K_ITEMS) {
-                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                const int kk = min(kb + key, nkv - 1);
-                kreg[n] = *reinterpret_cast<const uint4 *>(kbase + (size_t)kk * D + d0);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NVI; n++) {
-            const int item = tid + n * NT;
-            if (item < V_ITEMS) {
-                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                const int k0 = min(kb + 2 * kp, nkv - 1), k1 = min(kb + 2 * kp + 1, nkv - 1);
-                vreg[n][0] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k0 * D + d0);
-                vreg[n][1] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k1 * D + d0);
-            } else {
-                vreg[n][0] = uint4{0u, 0u, 0u, 0u};
-                vreg[n][1] = uint4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    // Largest |V| of the block just loaded, per wave, into s_wmax[buf].
-    auto publish_vmax = [&](int buf) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int n = 0; n < NVI; n++) m = max(m, max(max_mag8(vreg[n][0]), max_mag8(vreg[n][1])));
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-        if (lane == 0) s_wmax[buf][wave] = m;
-    };
-    // K as is; V transposed and converted to fp16 times 2^-vs, with vs chosen
-    // from the block's largest |V| so that the scaled values stay below 2^15.
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int n = 0; n < NKI; n++) {
-            const int item = tid + n * NT;
-            if (item < K_ITEMS) {
-                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&s_k[buf][key * KROW + d0]) = kreg[n];
-            }
-        }
-        uint32_t mb = 0;
-#pragma unroll
-        for (int w = 0; w < NW; w++) mb = max(mb, s_wmax[buf][w]);
-        const int ebits = (int)(mb >> 7);                       // bf16 biased exponent
-        const int vs = mb == 0 ? 0 : min(max(ebits - 141, -100), 15);
-        const float vscale = __builtin_ldexpf(1.0f, -vs);
-        if (tid == 0) s_vs[buf] = vs;
-#pragma unroll
-        for (int n = 0; n < NVI; n++) {
-            const int item = tid + n * NT;
-            if (item < V_ITEMS) {
-                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint32_t w = bf16_to_f16_scaled(half_of(vreg[n][0], e), vscale) |
-                                       (bf16_to_f16_scaled(half_of(vreg[n][1], e), vscale) << 16);
-                    *reinterpret_cast<uint32_t *>(&s_vt[buf][(d0 + e) * VROW + 2 * kp]) = w;
-                }
-            }
-        }
-    };
-
     f32x4 acc[NQT][DT];          // O^T in units of 2^-vs_cur
     float m_run[NQT], l_run[NQT];
 #pragma unroll
@@ -308,50 +334,38 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
     }
     int vs_cur = 0;
 
-    const int nblocks = (kend - kbeg + KB - 1) / KB;
-    if (nblocks > 0) {
-        gload(kbeg);
-        publish_vmax(0);
-    }
-    __syncthreads();
-    if (nblocks > 0) lstore(0);
-    __syncthreads();
-
-    for (int b = 0; b < nblocks; b++) {
-        const int buf = b & 1;
-        const int kb = kbeg + b * KB;
-        if (b + 1 < nblocks) gload(kb + KB);
-
-        bf16x8 kop[2][DS];
-#pragma unroll
-        for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-            for (int ds = 0; ds < DS; ds++)
-                kop[kt][ds] = *reinterpret_cast<const bf16x8 *>(&s_k[buf][(kt * 16 + l16) * KROW + ds * 32 + grp * 8]);
-        f16x8 vop[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-            const uint16_t *vr = &s_vt[buf][(dt * 16 + l16) * VROW];
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr + grp * 4);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + grp * 4);
-            vop[dt] = __builtin_bit_cast(f16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-        }
+    auto compute = [=](int kb, int buf, f32x4 (&acc)[NQT][DT], float (&m_run)[NQT], float (&l_run)[NQT],
+                       int &vs_cur) __attribute__((always_inline)) {
         const int vs_blk = s_vs[buf];
         const float vfix = __builtin_ldexpf(1.0f, vs_cur - vs_blk);   // re-express acc in 2^-vs_blk
         const bool vchange = vs_blk != vs_cur;
         vs_cur = vs_blk;
         const bool masked = (kb + KB > P) || (kb + KB > kend);
 
+        // S^T tiles of every query tile: K operands loaded one key tile at a time.
+        f32x4 S[NQT][2];
+#pragma unroll
+        for (int t = 0; t < NQT; t++) S[t][0] = S[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+            bf16x8 kop[DS];
+#pragma unroll
+            for (int ds = 0; ds < DS; ds++)
+                kop[ds] = *reinterpret_cast<const bf16x8 *>(&s_k[buf][(kt * 16 + l16) * KROW + ds * 32 + grp * 8]);
+#pragma unroll
+            for (int ds = 0; ds < DS; ds++)
+#pragma unroll
+                for (int t = 0; t < NQT; t++)
+                    S[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds], qop[t][ds], S[t][kt], 0, 0, 0);
+        }
+
+        // Online softmax per query column; P^T operands in fp16.
+        f16x8 pop[NQT];
 #pragma unroll
         for (int t = 0; t < NQT; t++) {
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ds = 0; ds < DS; ds++) {
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][ds], qop[t][ds], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][ds], qop[t][ds], s1, 0, 0, 0);
-            }
             // sv[e]: key kb + grp*4 + e (e < 4) or kb + 16 + grp*4 + (e - 4)
-            float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+            float sv[8] = {S[t][0][0], S[t][0][1], S[t][0][2], S[t][0][3],
+                           S[t][1][0], S[t][1][1], S[t][1][2], S[t][1][3]};
             if (masked) {
                 const unsigned *anc = &s_anc[qnode[t] * 8];
 #pragma unroll
@@ -386,23 +400,60 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) acc[t][dt] *= f;
             }
-            const f16x8 pop = pack_f16x8(pv);
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++)
-                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[dt], pop, acc[t][dt], 0, 0, 0);
+            pop[t] = pack_f16x8(pv);
         }
 
-        if (b + 1 < nblocks) {
-            publish_vmax(buf ^ 1);
-            __syncthreads();          // all waves are done reading buffer buf ^ 1
-            lstore(buf ^ 1);
-            __syncthreads();
+        // O^T += V^T P^T: V operands loaded one d-tile at a time.
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) {
+            const uint16_t *vr = &s_vt[buf][(dt * 16 + l16) * VROW];
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vr + grp * 4);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + grp * 4);
+            const f16x8 vop = __builtin_bit_cast(f16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+            for (int t = 0; t < NQT; t++)
+                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[t], acc[t][dt], 0, 0, 0);
         }
+    };
+
+    // Block 0 into LDS buffer 0 (the tree bitmap above is also published here).
+    if (nblocks > 0) publish_vmax(vreg0, s_wmax[0]);
+    __syncthreads();
+    if (nblocks > 0) lstore(kreg0, vreg0, s_k[0], s_vt[0], s_wmax[0], &s_vs[0]);
+    __syncthreads();
+
+    // Block b sits in register slot b % PD until it is written to LDS buffer
+    // b & 1 at the end of iteration b - 1; its slot is then refilled with block
+    // b + PD at the start of iteration b.
+    // One pipeline stage: block b = b0 + SL lives in stage SL's registers; NX is
+    // the stage that holds block b + 1.
+#define TEV_ATTN_STAGE(SL, NX)                                                                  \
+    {                                                                                           \
+        const int b = b0 + (SL);                                                                \
+        if (b < nblocks) {                                                                      \
+            if (b + PD < nblocks) gload(kreg##SL, vreg##SL, kbeg + (b + PD) * KB);              \
+            compute(kbeg + b * KB, b & 1, acc, m_run, l_run, vs_cur);                           \
+            if (b + 1 < nblocks) {                                                              \
+                const int nb = (b + 1) & 1;                                                     \
+                publish_vmax(vreg##NX, s_wmax[nb]);                                             \
+                __syncthreads(); /* all waves are done reading buffer nb */                     \
+                lstore(kreg##NX, vreg##NX, s_k[nb], s_vt[nb], s_wmax[nb], &s_vs[nb]);           \
+                __syncthreads();                                                                \
+            }                                                                                   \
+        }                                                                                       \
     }
+    static_assert(PD == 4, "the pipeline below is written out for four register stages");
+    for (int b0 = 0; b0 < nblocks; b0 += PD) {
+        TEV_ATTN_STAGE(0, 1)
+        TEV_ATTN_STAGE(1, 2)
+        TEV_ATTN_STAGE(2, 3)
+        TEV_ATTN_STAGE(3, 0)
+    }
+#undef TEV_ATTN_STAGE
     const float vunscale = __builtin_ldexpf(1.0f, vs_cur);
 
     // Finalise: the four lanes of a query column hold disjoint key subsets.
-    const size_t rows_all = (size_t)gridDim.z * rows_total;
+    const size_t rows_all = (size_t)(n_wg / (row_blocks * splits)) * rows_total;
 #pragma unroll
     for (int t = 0; t < NQT; t++) {
         float lt = l_run[t];
@@ -433,35 +484,56 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(
     }
 }
 
-// Merge split partials: grid over (kv row, d).
+constexpr int MAX_SPLITS = 32;
+
+// Merge split partials: one wave per query row (grid ceil(rows_all / 4), 256
+// threads); lane s reads split s's (m, l), every lane its D/64 output
+// columns of all splits, all loads issued before the first use.
+template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml,
                                                       int splits, int Hkv, int G, int B, int Hq,
-                                                      int D, size_t rows_all,
+                                                      size_t rows_all,
                                                       const unsigned *__restrict__ status,
                                                       float *__restrict__ out) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= rows_all * D) return;
-    const size_t row = idx / D;
-    const int d = (int)(idx - row * D);
+    constexpr int DPL = D / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t row = (size_t)blockIdx.x * 4 + wave;
+    if (row >= rows_all) return;
     const int rows_total = G * B;
     const int rg = (int)(row / rows_total);
     const int rr = (int)(row - (size_t)rg * rows_total);
     const int r = rg / Hkv, g = rg - r * Hkv;
     const int i = rr / G, hh = rr - i * G;
-    float M = -kInf;
-    for (int s = 0; s < splits; s++) M = fmaxf(M, part_ml[((size_t)s * rows_all + row) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < splits; s++) {
-        const size_t pr = (size_t)s * rows_all + row;
-        const float ms = part_ml[pr * 2];
-        const float f = (ms > -kInf) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
-        L += part_ml[pr * 2 + 1] * f;
-        O += part_o[pr * D + d] * f;
+    float ms = -kInf, ls = 0.f;
+    if (lane < splits) {
+        ms = part_ml[((size_t)lane * rows_all + row) * 2];
+        ls = part_ml[((size_t)lane * rows_all + row) * 2 + 1];
     }
-    float res = O / L;
-    if (status[r] != 0u) res = __builtin_nanf("");
-    out[(((size_t)r * B + i) * Hq + g * G + hh) * D + d] = res;
+    float o[MAX_SPLITS][DPL];
+#pragma unroll
+    for (int s = 0; s < MAX_SPLITS; s++)
+#pragma unroll
+        for (int j = 0; j < DPL; j++)
+            o[s][j] = (s < splits) ? part_o[((size_t)s * rows_all + row) * D + lane * DPL + j] : 0.f;
+    const float M = wave::max_f32(ms);
+    const float wgt = (ms > -kInf) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+    const float L = wave::sum_f32(ls * wgt);
+    float acc[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; j++) acc[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < MAX_SPLITS; s++) {
+        if (s < splits) {
+            const float ws = wave::readlane_f(wgt, s);
+#pragma unroll
+            for (int j = 0; j < DPL; j++) acc[j] = fmaf(ws, o[s][j], acc[j]);
+        }
+    }
+    const bool bad = status[r] != 0u;
+    float *dst = out + (((size_t)r * B + i) * Hq + g * G + hh) * D + lane * DPL;
+#pragma unroll
+    for (int j = 0; j < DPL; j++) dst[j] = bad ? __builtin_nanf("") : acc[j] / L;
 }
 
 template <int D, int NQT, int NW>
@@ -473,15 +545,16 @@ hipError_t mfma_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     float *part_o = (float *)(ws + L.part_o);
     float *part_ml = (float *)(ws + L.part_ml);
     unsigned *status = (unsigned *)(ws + L.status);
-    k_attn_mfma<D, NQT, NW><<<dim3(pl.row_blocks, pl.splits, R * Hkv), NW * 64, 0, st>>>(
-        q, k, v, parents, B, Hq, Hkv, P, c_log2, pl.splits, pl.keys_per_split, out, part_o,
-        part_ml, status);
+    const int n_wg = pl.row_blocks * pl.splits * R * Hkv;
+    const int grid = 8 * ((n_wg + 7) / 8);
+    k_attn_mfma<D, NQT, NW><<<dim3(grid), NW * 64, 0, st>>>(
+        q, k, v, parents, B, Hq, Hkv, P, c_log2, pl.row_blocks, pl.splits, pl.keys_per_split, n_wg,
+        out, part_o, part_ml, status);
     if (pl.splits > 1) {
         const int G = Hq / Hkv;
         const size_t rows_all = (size_t)R * Hkv * G * B;
-        const size_t n = rows_all * D;
-        k_attn_combine<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(
-            part_o, part_ml, pl.splits, Hkv, G, B, Hq, D, rows_all, status, out);
+        k_attn_combine<D><<<dim3((unsigned)((rows_all + 3) / 4)), 256, 0, st>>>(
+            part_o, part_ml, pl.splits, Hkv, G, B, Hq, rows_all, status, out);
     }
     return hipGetLastError();
 }
@@ -502,6 +575,7 @@ AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P) {
     long want = (512 + base - 1) / base;
     long maxs = P / 256;
     if (maxs < 1) maxs = 1;
+    if (maxs > MAX_SPLITS) maxs = MAX_SPLITS;
     int S = (int)(want < maxs ? want : maxs);
     if (S < 1) S = 1;
     int kps = 0;

@@ -132,7 +132,7 @@ def tev_exit_law(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tens
     need = tev_exit_law_workspace_bytes(R, B, V)
     if out is None:
         if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
         out = ExitLawResult(torch.empty((R, B), dtype=torch.float32, device=dev),
                             torch.empty((R, B), dtype=torch.float32, device=dev),
                             torch.empty((R, B), dtype=torch.float32, device=dev),
@@ -183,7 +183,7 @@ def tev_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: to
         scale = 1.0 / float(np.sqrt(D))
     need = tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((R, B, Hq, D), dtype=torch.float32, device=q.device)
     st = lib().tev_tree_attn(_p(q), _p(k), _p(v), _dtype_code(q), _p(parents), R, B, Hq, Hkv, D,

@@ -83,10 +83,11 @@ typedef enum { TEV_F32 = 0, TEV_BF16 = 1 } tev_dtype;
  *           is a multiple of 16 bytes and `logits` is 16-byte aligned.
  * rho, reach, exit_mass  float [R][B] outputs;  coverage float [R] output.
  * inv_temperature must be finite and > 0 (1.0 = the target's own law).
- * workspace must hold tev_exit_law_workspace_bytes(R, B, V) bytes; after the
- * call it holds the fp64 exit law and per-chunk row statistics that
- * tev_sample reads.  Its contents are private.
- * Each row of logits is read exactly once.
+ * workspace must hold tev_exit_law_workspace_bytes(R, B, V) bytes (any
+ * initial contents).  After the call it holds the fp64 exit law and
+ * per-chunk row statistics that tev_sample reads.  Its contents are private.
+ * Calls that share a workspace must not overlap in time.  Each row of logits
+ * is read exactly once.
  * ------------------------------------------------------------------------ */
 size_t tev_exit_law_workspace_bytes(int R, int B, int V);
 

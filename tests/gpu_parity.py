@@ -128,7 +128,7 @@ def run_attn(wl):
     q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
     assert q.dtype == dt
     par = tev.to_device_i32(wl.parents)
-    ws = torch.empty(max(1, tev.tev_tree_attn_workspace_bytes(wl.R, wl.B, wl.Hq, wl.Hkv, wl.D, wl.P)),
+    ws = torch.zeros(max(1, tev.tev_tree_attn_workspace_bytes(wl.R, wl.B, wl.Hq, wl.Hkv, wl.D, wl.P)),
                      dtype=torch.uint8, device="cuda")
     out = tev.tev_tree_attn(q, k, v, par, wl.P, wl.scale, workspace=ws)
     torch.cuda.synchronize()

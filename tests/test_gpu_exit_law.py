@@ -1,5 +1,5 @@
 """GPU parity of tev_exit_law and tev_sample against the CPU oracle (called
-through the C ABI).  Small cases span several 8192-token chunks and a ragged
+through the C ABI).  Small cases span several 4096-token chunks and a ragged
 tail; the named workloads run at full size."""
 import numpy as np
 import pytest
@@ -131,3 +131,24 @@ def test_determinism_bitwise():
     ca = tev.tev_export_exit_cdf(a["res"].workspace, wl.R, wl.B, wl.V)
     cb = tev.tev_export_exit_cdf(b["res"].workspace, wl.R, wl.B, wl.V)
     np.testing.assert_array_equal(ca, cb)
+
+
+def test_workspace_reuse_across_calls():
+    """One zero-filled workspace serves consecutive calls: every call leaves
+    its completion counters at zero again."""
+    import torch
+    wls = [W.make_custom(f"reuse{i}", R=2, B=33, V=30000, dtype="bf16", tree="random", seed=200 + i,
+                         with_attention=False, n_uniform=128) for i in range(3)]
+    ws = torch.zeros(tev.tev_exit_law_workspace_bytes(2, 33, 30000), dtype=torch.uint8, device="cuda")
+    for wl in wls * 2:
+        lg, par, tok, uni = GP.device_inputs(wl)
+        res = tev.tev_exit_law(lg, par, tok, 1.0, workspace=ws)
+        en, bt = tev.tev_sample(lg, par, tok, res.workspace, uni)
+        torch.cuda.synchronize()
+        ora = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens)
+        GP.assert_close_rel("w", res.exit_mass.cpu().numpy(), ora.exit_mass)
+        GP.assert_close_rel("C", res.coverage.cpu().numpy(), ora.coverage)
+        dr = oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, ora.exit_mass, wl.uniforms)
+        ok = ~(dr.band_exit | dr.band_bonus)
+        assert np.array_equal(en.cpu().numpy()[ok], dr.exit_node[ok])
+        assert np.array_equal(bt.cpu().numpy()[ok], dr.bonus_token[ok])
