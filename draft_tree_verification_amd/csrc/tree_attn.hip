@@ -42,6 +42,11 @@ constexpr float kInf = __builtin_inff();
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Plain clang vectors for 16- and 8-byte moves: unlike HIP's u32x4 struct they
+// stay in registers (struct copies become memcpy that the compiler keeps in
+// memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
@@ -131,9 +136,11 @@ __global__ __launch_bounds__(256) void k_attn_alu(const float *__restrict__ q,
 // bf16 MFMA kernel.
 // ----------------------------------------------------------------------------
 constexpr int KB = 32;   // keys per block
+constexpr int kVsMin = -100;     // smallest V exponent shift (all-zero blocks)
+constexpr float kLazy = 8.0f;    // slack of the softmax reference max (log2 units)
 
-__device__ __forceinline__ uint32_t half_of(const uint4 &x, int e) {
-    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+__device__ __forceinline__ uint32_t half_of(const u32x4 &x, int e) {
+    const uint32_t w = x[e >> 1];
     return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
@@ -154,11 +161,10 @@ __device__ __forceinline__ uint32_t bf16_to_f16_scaled(uint32_t b, float scale) 
 
 // Largest |value| of the 8 bf16 in x, as a 15-bit magnitude pattern (the
 // ordering of non-negative IEEE patterns is the ordering of the values).
-__device__ __forceinline__ uint32_t max_mag8(const uint4 &x) {
+__device__ __forceinline__ uint32_t max_mag8(const u32x4 &x) {
     uint32_t m = 0;
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i = 0; i < 4; i++) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    for (int i = 0; i < 4; i++) m = max(m, max(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
     return m;
 }
 
@@ -208,7 +214,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __shared__ unsigned s_anc[TEV_MAX_NODES * 8];
     __shared__ int s_par[TEV_MAX_NODES];
     __shared__ uint32_t s_wmax[2][NW];
-    __shared__ int s_vs[2];
     __shared__ int s_bad;
 
     const bool last = (sp == splits - 1);
@@ -220,64 +225,66 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int nblocks = (kend - kbeg + KB - 1) / KB;
 
     // PD register stages, one named array pair per stage
-    uint4 kreg0[NKI], kreg1[NKI], kreg2[NKI], kreg3[NKI];
-    uint4 vreg0[NVI][2], vreg1[NVI][2], vreg2[NVI][2], vreg3[NVI][2];
-    auto gload = [=](uint4 (&kr)[NKI], uint4 (&vr)[NVI][2], int kb) __attribute__((always_inline)) {
+    u32x4 kreg0[NKI], kreg1[NKI], kreg2[NKI], kreg3[NKI];
+    u32x4 vreg0[NVI][2], vreg1[NVI][2], vreg2[NVI][2], vreg3[NVI][2];
+    auto gload = [=](u32x4 (&kr)[NKI], u32x4 (&vr)[NVI][2], int kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < NKI; n++) {
             const int item = tid + n * NT;
             if (K_FULL || item < K_ITEMS) {
                 const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
                 const int kk = min(kb + key, nkv - 1);
-                kr[n] = *reinterpret_cast<const uint4 *>(kbase + (size_t)kk * D + d0);
+                kr[n] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)kk * D + d0);
             }
         }
 #pragma unroll
         for (int n = 0; n < NVI; n++) {
             const int item = tid + n * NT;
             if (V_FULL || item < V_ITEMS) {
-                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
+                const int kp = item % (KB / 2), d0 = (item / (KB / 2)) * 8;
                 const int k0 = min(kb + 2 * kp, nkv - 1), k1 = min(kb + 2 * kp + 1, nkv - 1);
-                vr[n][0] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k0 * D + d0);
-                vr[n][1] = *reinterpret_cast<const uint4 *>(vbase + (size_t)k1 * D + d0);
+                vr[n][0] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)k0 * D + d0);
+                vr[n][1] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)k1 * D + d0);
             } else {
-                vr[n][0] = uint4{0u, 0u, 0u, 0u};
-                vr[n][1] = uint4{0u, 0u, 0u, 0u};
+                vr[n][0] = u32x4{0u, 0u, 0u, 0u};
+                vr[n][1] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
     // Largest |V| of the block held in register slot sl, per wave, into s_wmax[buf].
-    auto publish_vmax = [=](const uint4 (&vr)[NVI][2], uint32_t *wmax) __attribute__((always_inline)) {
+    auto publish_vmax = [=](const u32x4 (&vr)[NVI][2], uint32_t *wmax) __attribute__((always_inline)) {
         uint32_t m = 0;
 #pragma unroll
         for (int n = 0; n < NVI; n++) m = max(m, max(max_mag8(vr[n][0]), max_mag8(vr[n][1])));
         m = (uint32_t)wave::max_i32((int)m);
         if (lane == 0) wmax[wave] = m;
     };
-    // K as is; V transposed and converted to fp16 times 2^-vs, with vs chosen
-    // from the block's largest |V| so that the scaled values stay below 2^15.
-    auto lstore = [=](const uint4 (&kr)[NKI], const uint4 (&vr)[NVI][2], uint16_t *sk, uint16_t *svt,
-                      const uint32_t *wmax, int *vs_out) __attribute__((always_inline)) {
+    // K as is; V transposed and converted to fp16 times 2^-vs.  vs is the
+    // smallest exponent seen so far that keeps every scaled |V| below 2^15: it
+    // only ever grows, so the accumulators change units only when a block with
+    // larger values arrives.
+    auto lstore = [=](const u32x4 (&kr)[NKI], const u32x4 (&vr)[NVI][2], uint16_t *sk, uint16_t *svt,
+                      const uint32_t *wmax, int &vs_run) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < NKI; n++) {
             const int item = tid + n * NT;
             if (K_FULL || item < K_ITEMS) {
                 const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&sk[key * KROW + d0]) = kr[n];
+                *reinterpret_cast<u32x4 *>(&sk[key * KROW + d0]) = kr[n];
             }
         }
         uint32_t mb = 0;
 #pragma unroll
         for (int w = 0; w < NW; w++) mb = max(mb, wmax[w]);
         const int ebits = (int)(mb >> 7);                       // bf16 biased exponent
-        const int vs = mb == 0 ? 0 : min(max(ebits - 141, -100), 15);
-        const float vscale = __builtin_ldexpf(1.0f, -vs);
-        if (tid == 0) *vs_out = vs;
+        const int vs_need = mb == 0 ? kVsMin : min(max(ebits - 141, kVsMin), 15);
+        vs_run = max(vs_run, vs_need);
+        const float vscale = __builtin_ldexpf(1.0f, -vs_run);
 #pragma unroll
         for (int n = 0; n < NVI; n++) {
             const int item = tid + n * NT;
             if (V_FULL || item < V_ITEMS) {
-                const int kp = item / (D / 8), d0 = (item % (D / 8)) * 8;
+                const int kp = item % (KB / 2), d0 = (item / (KB / 2)) * 8;
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
                     const uint32_t w = bf16_to_f16_scaled(half_of(vr[n][0], e), vscale) |
@@ -288,26 +295,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         }
     };
 
-    // Prefetch the first PD blocks before anything else.
-    if (0 < nblocks) gload(kreg0, vreg0, kbeg);
-    if (1 < nblocks) gload(kreg1, vreg1, kbeg + KB);
-    if (2 < nblocks) gload(kreg2, vreg2, kbeg + 2 * KB);
-    if (3 < nblocks) gload(kreg3, vreg3, kbeg + 3 * KB);
-
-    bool tree_ok = true;
-    if (last) {
-        tree_ok = load_parents(parents + (size_t)r * B, B, s_par, &s_bad);
-        if (tree_ok) {
-            for (int i = tid; i < B; i += NT) {
-#pragma unroll
-                for (int w = 0; w < 8; w++) s_anc[i * 8 + w] = 0u;
-                for (int j = i; j >= 0; j = s_par[j]) s_anc[i * 8 + (j >> 5)] |= 1u << (j & 31);
-            }
-        }
-        if (rb == 0 && g == 0 && tid == 0) status[r] = tree_ok ? 0u : TEV_FLAG_TREE;
-    }
-
-    // This lane's query column in each of its NQT tiles, and its Q^T operands.
+    // Issue order: Q^T operands and the request's parents first, then the K/V
+    // prefetch, so that waiting for the small loads never waits for the stream.
     bf16x8 qop[NQT][DS];
     int qnode[NQT], qrow[NQT];
 #pragma unroll
@@ -320,7 +309,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const uint16_t *qp = q + (((size_t)r * B + i) * Hq + g * G + hh) * D;
 #pragma unroll
         for (int ds = 0; ds < DS; ds++)
-            qop[t][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(qp + ds * 32 + grp * 8));
+            qop[t][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + ds * 32 + grp * 8));
+    }
+    constexpr int NPAR = (TEV_MAX_NODES + NT - 1) / NT;
+    int my_par[NPAR];
+#pragma unroll
+    for (int n = 0; n < NPAR; n++) {
+        const int i = tid + n * NT;
+        my_par[n] = (last && i < B) ? parents[(size_t)r * B + i] : -1;
+    }
+
+    if (0 < nblocks) gload(kreg0, vreg0, kbeg);
+    if (1 < nblocks) gload(kreg1, vreg1, kbeg + KB);
+    if (2 < nblocks) gload(kreg2, vreg2, kbeg + 2 * KB);
+    if (3 < nblocks) gload(kreg3, vreg3, kbeg + 3 * KB);
+
+    // Tree contract (parents[0] = -1, 0 <= parents[i] < i) and the ancestor
+    // bitmap of every node (bit j of node i: j lies on i's root path).
+    bool tree_ok = true;
+    if (last) {
+        if (tid == 0) s_bad = 0;
+#pragma unroll
+        for (int n = 0; n < NPAR; n++) {
+            const int i = tid + n * NT;
+            if (i < B) s_par[i] = my_par[n];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NPAR; n++) {
+            const int i = tid + n * NT, p = my_par[n];
+            if (i < B && !((i == 0) ? (p == -1) : (p >= 0 && p < i))) s_bad = 1;
+        }
+        __syncthreads();
+        tree_ok = s_bad == 0;
+        if (tree_ok) {
+#pragma unroll
+            for (int n = 0; n < NPAR; n++) {
+                const int i = tid + n * NT;
+                if (i >= B) continue;
+                unsigned a[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+                for (int j = i; j >= 0; j = s_par[j]) {
+#pragma unroll
+                    for (int w = 0; w < 8; w++) a[w] |= ((j >> 5) == w) ? (1u << (j & 31)) : 0u;
+                }
+#pragma unroll
+                for (int w = 0; w < 8; w++) s_anc[i * 8 + w] = a[w];
+            }
+        }
+        if (rb == 0 && g == 0 && tid == 0) status[r] = tree_ok ? 0u : TEV_FLAG_TREE;
     }
 
     f32x4 acc[NQT][DT];          // O^T in units of 2^-vs_cur
@@ -332,11 +368,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    int vs_cur = 0;
+    int vs_cur = kVsMin;   // unit of acc: 2^-vs_cur
+    int vs_run = kVsMin;   // unit of the V block last written to LDS
 
     auto compute = [=](int kb, int buf, f32x4 (&acc)[NQT][DT], float (&m_run)[NQT], float (&l_run)[NQT],
-                       int &vs_cur) __attribute__((always_inline)) {
-        const int vs_blk = s_vs[buf];
+                       int &vs_cur, const int vs_blk) __attribute__((always_inline)) {
         const float vfix = __builtin_ldexpf(1.0f, vs_cur - vs_blk);   // re-express acc in 2^-vs_blk
         const bool vchange = vs_blk != vs_cur;
         vs_cur = vs_blk;
@@ -383,9 +419,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
             for (int e = 1; e < 8; e++) bm = fmaxf(bm, sv[e]);
             bm = fmaxf(bm, __shfl_xor(bm, 16));
             bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float m_new = fmaxf(m_run[t], bm * c_log2);
+            // The reference max moves only when the block's max exceeds it by
+            // more than kLazy (log2 units): probabilities stay <= 2^kLazy, exact
+            // in fp16, and the accumulators are rescaled only when it moves.
+            const float bmc = bm * c_log2;
+            const bool grow = bmc > m_run[t] + kLazy;
+            const float m_new = grow ? bmc : m_run[t];
             const float m_use = (m_new == -kInf) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_use);
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[t] - m_use) : 1.0f;
             float pv[8];
             float ps = 0.f;
 #pragma unroll
@@ -395,7 +436,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
             }
             l_run[t] = l_run[t] * alpha + ps;
             m_run[t] = m_new;
-            if (vchange || __any(alpha != 1.0f)) {
+            if (vchange || __any(grow)) {
                 const float f = alpha * vfix;
 #pragma unroll
                 for (int dt = 0; dt < DT; dt++) acc[t][dt] *= f;
@@ -407,9 +448,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
             const uint16_t *vr = &s_vt[buf][(dt * 16 + l16) * VROW];
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr + grp * 4);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16 + grp * 4);
-            const f16x8 vop = __builtin_bit_cast(f16x8, uint4{lo.x, lo.y, hi.x, hi.y});
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + grp * 4);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 + grp * 4);
+            const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
             for (int t = 0; t < NQT; t++)
                 acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[t], acc[t][dt], 0, 0, 0);
@@ -419,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // Block 0 into LDS buffer 0 (the tree bitmap above is also published here).
     if (nblocks > 0) publish_vmax(vreg0, s_wmax[0]);
     __syncthreads();
-    if (nblocks > 0) lstore(kreg0, vreg0, s_k[0], s_vt[0], s_wmax[0], &s_vs[0]);
+    if (nblocks > 0) lstore(kreg0, vreg0, s_k[0], s_vt[0], s_wmax[0], vs_run);
     __syncthreads();
 
     // Block b sits in register slot b % PD until it is written to LDS buffer
@@ -432,12 +473,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int b = b0 + (SL);                                                                \
         if (b < nblocks) {                                                                      \
             if (b + PD < nblocks) gload(kreg##SL, vreg##SL, kbeg + (b + PD) * KB);              \
-            compute(kbeg + b * KB, b & 1, acc, m_run, l_run, vs_cur);                           \
+            compute(kbeg + b * KB, b & 1, acc, m_run, l_run, vs_cur, vs_run);                   \
             if (b + 1 < nblocks) {                                                              \
                 const int nb = (b + 1) & 1;                                                     \
                 publish_vmax(vreg##NX, s_wmax[nb]);                                             \
                 __syncthreads(); /* all waves are done reading buffer nb */                     \
-                lstore(kreg##NX, vreg##NX, s_k[nb], s_vt[nb], s_wmax[nb], &s_vs[nb]);           \
+                lstore(kreg##NX, vreg##NX, s_k[nb], s_vt[nb], s_wmax[nb], vs_run);              \
                 __syncthreads();                                                                \
             }                                                                                   \
         }                                                                                       \
