@@ -14,25 +14,27 @@
 // of the row's child tokens) and a child part.  Each logit is read exactly
 // once: this pass is HBM-bound.
 //
-// k_reach -- one workgroup of 512 threads per request:
-//   row pass (8 waves, rows dealt round-robin, four rows' chunk partials in
-//   flight per wave): fixed-order fp64 combine of the row's chunk sums and the
-//   running residual sums the sampler searches; rho by masking, never by
-//   subtraction.
+// k_reach -- one workgroup of 1024 threads per request:
+//   row pass (16 waves, rows dealt round-robin, a batch of four rows' chunk
+//   partials loaded together, the next batch issued before this one's
+//   stores): fixed-order fp64 combine of the row's chunk sums and the running
+//   residual sums the sampler searches; rho by masking, never by subtraction.
 //   tree pass (wave 0, on the row results in LDS): child probabilities in
-//   fp64, the reach P level by level (Algorithm 1's loop over depth, one
-//   wave-level LDS sync per level), w, C and the exit CDF.
+//   fp64 (their logits gathered while the row pass runs), the reach P by
+//   pointer jumping along root paths, w, C and the exit CDF.
 //
-// k_sample -- one wave per (draw, request): exit draw over the node CDF,
-// chunk search over the row's running residual sums, then an fp64 wave scan
-// inside the one chunk that holds the bonus token.
+// k_sample -- one wave per (draw, request), loads in three dependent rounds:
+// exit draw over the node CDF, chunk search over the row's running residual
+// sums, then an fp64 wave scan inside the one chunk that holds the bonus
+// token.
 //
 // Numerics: sL = fl(s * log2 e); each element contributes
-// 2^(fma(l, sL, -M_c)) with one rounding of the shifted exponent, M_c being a
-// per-chunk f32 offset that cancels exactly in the fp64 combine.  Chunk and
-// row combines, child probabilities, P, w, C and both CDFs are fp64.  All
-// reductions run in a fixed order (no float atomics): results are
-// bit-reproducible.
+// 2^(fma(l, sL, -M_c)) with one rounding of the shifted exponent, M_c being
+// an integer-valued per-chunk f32 offset (the floor of the chunk's largest
+// l * sL), so that every term is below 2 and moving a chunk sum to another
+// offset is an exact power of two.  Chunk and row combines, child
+// probabilities, P, w, C and both CDFs are fp64.  All reductions run in a
+// fixed order (no float atomics): results are bit-reproducible.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -143,7 +145,9 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
 #pragma unroll
     for (int j = 1; j < EPT; j++) m = fmaxf(m, x[j]);
     m = wave::max_f32(m);
-    const float Mc = m * sL;
+    // Integer offset: every term is below 2, and rescaling between chunk
+    // offsets is an exact power of two.
+    const float Mc = floorf(m * sL);
     double accR = 0.0, accC = 0.0;
     if (m > -kInf) {
         if (!wave_has_children) {
@@ -200,12 +204,20 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
 // ----------------------------------------------------------------------------
 // k_reach.
 // ----------------------------------------------------------------------------
-constexpr int REACH_THREADS = 512;
+constexpr int REACH_THREADS = 1024;
 constexpr int REACH_WAVES = REACH_THREADS / 64;
-constexpr int ROW_BATCH = 4;        // rows whose partials a wave keeps in flight
-constexpr int FAST_NC = 128;        // chunks per row held in registers (2 per lane)
+constexpr int ROW_BATCH = 4;        // rows per wave whose partials are loaded together
+constexpr int FAST_NC = 64;         // chunks per row held in registers (one per lane)
+constexpr int MAX_BATCHES = (TEV_MAX_NODES + REACH_WAVES * ROW_BATCH - 1) / (REACH_WAVES * ROW_BATCH);
 
-template <typename T>
+// 2^e for an integer-valued e <= 0 (chunk offsets are integers): exact.
+__device__ __forceinline__ double pow2_int(float e) {
+    return __builtin_ldexp(1.0, (int)fmaxf(e, -2000.f));
+}
+
+// NB = ceil(B / (REACH_WAVES * ROW_BATCH)) batches, a template parameter so
+// that every load of the pipeline is unconditional.
+template <typename T, int NB>
 __global__ __launch_bounds__(REACH_THREADS) void k_reach(
     const T *__restrict__ logits, const int32_t *__restrict__ parents,
     const int32_t *__restrict__ tokens, int B, int V, int nc, float sL, ExitPtrs W,
@@ -214,108 +226,137 @@ __global__ __launch_bounds__(REACH_THREADS) void k_reach(
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    __shared__ int s_par[TEV_MAX_NODES];
+    __shared__ int s_anc[TEV_MAX_NODES];
     __shared__ float s_M[TEV_MAX_NODES];
     __shared__ double s_Z[TEV_MAX_NODES];
     __shared__ double s_rho[TEV_MAX_NODES];
-    __shared__ double s_P[TEV_MAX_NODES];
+    __shared__ double s_prod[TEV_MAX_NODES];
     __shared__ unsigned s_flags;
     const size_t rb0 = (size_t)r * B;
+    const bool fast = nc <= FAST_NC;
 
+    // Issue order: the tree arrays, then this wave's first batch of chunk
+    // partials, then (once parents and tokens are in) the child-logit
+    // gathers; no global store is issued before the last load.
+    // Every load below is unconditional (out-of-range lanes read a clamped,
+    // valid address and discard the value): conditional loads would make the
+    // compiler wait for all outstanding loads where the branches join.
+    const bool mine = tid < B;
+    const int ti = min(tid, B - 1);
+    const int pa = parents[rb0 + ti];
+    const int tk = tokens[rb0 + ti];
+    float pm[2][ROW_BATCH];
+    unsigned pf[2][ROW_BATCH];
+    double pr[2][ROW_BATCH], pcs[2][ROW_BATCH];
+    // Loads the partials of batch BT (rows wave + REACH_WAVES * (ROW_BATCH * BT + q)) into buffer BUF.
+#define TEV_REACH_LOAD(BUF, BT)                                                                 \
+    {                                                                                           \
+        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
+            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
+            const bool ok = v < B && lane < nc;   /* masked where used; unused when !fast */   \
+            const size_t o = (rb0 + (ok ? v : 0)) * nc + (ok ? lane : 0);                       \
+            pm[BUF][q] = W.part_m[o];                                                           \
+            pf[BUF][q] = W.flags[o];                                                            \
+            pr[BUF][q] = W.part_r[o];                                                           \
+            pcs[BUF][q] = W.part_c[o];                                                          \
+        }                                                                                       \
+    }
+    TEV_REACH_LOAD(0, 0)
+    const bool bad = mine && ((tid == 0) ? (pa != -1) : (pa < 0 || pa >= tid || tk < 0 || tk >= V));
+    const bool child = mine && tid > 0 && !bad;
+    T lraw = logits[(rb0 + (child ? pa : 0)) * (size_t)V + (child ? tk : 0)];
     if (tid == 0) s_flags = 0u;
     __syncthreads();
-    // tree contract, one thread per node
-    if (tid < B) {
-        const int pa = parents[rb0 + tid];
-        const int tk = tokens[rb0 + tid];
-        const bool bad = (tid == 0) ? (pa != -1) : (pa < 0 || pa >= tid || tk < 0 || tk >= V);
-        s_par[tid] = bad ? 0 : pa;
-        if (bad) atomicOr(&s_flags, TEV_FLAG_TREE);
-    }
+    if (mine) s_anc[tid] = child ? pa : 0;
+    if (bad) atomicOr(&s_flags, TEV_FLAG_TREE);
 
-    // ---- row pass ----
-    for (int v0 = wave; v0 < B; v0 += REACH_WAVES * ROW_BATCH) {
-        float pm[ROW_BATCH][2];
-        unsigned pf[ROW_BATCH][2];
-        double pr[ROW_BATCH][2], pcs[ROW_BATCH][2];
-        const bool fast = nc <= FAST_NC;
-        if (fast) {
-#pragma unroll
-            for (int q = 0; q < ROW_BATCH; q++) {
-                const int v = v0 + q * REACH_WAVES;
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int cc = lane + 64 * h;
-                    const bool ok = v < B && cc < nc;
-                    const size_t o = (rb0 + (ok ? v : 0)) * nc + (ok ? cc : 0);
-                    pm[q][h] = ok ? W.part_m[o] : -kInf;
-                    pf[q][h] = ok ? W.flags[o] : 0u;
-                    pr[q][h] = ok ? W.part_r[o] : 0.0;
-                    pcs[q][h] = ok ? W.part_c[o] : 0.0;
-                }
-            }
+    // ---- row pass: per row the fp64 combine of its chunk partials ----
+    // chunk offsets are integers, so rescaling a partial to the row offset M
+    // is an exact power of two.
+    auto finish_row = [&](int v, float M, unsigned f, double carry, double csum) {
+        csum = wave::sum_f64(csum);
+        const double Z = carry + csum;
+        if (!(M > -kInf) || !(Z > 0.0) || isnan(Z)) f |= TEV_FLAG_NONFINITE;
+        if (lane == 0) {
+            s_M[v] = M;
+            s_Z[v] = Z;
+            s_rho[v] = carry / Z;
+            W.row_m[rb0 + v] = M;
+            if (f) atomicOr(&s_flags, f);
         }
-#pragma unroll
-        for (int q = 0; q < ROW_BATCH; q++) {
-            const int v = v0 + q * REACH_WAVES;
-            if (v >= B) break;
+    };
+    if (fast) {
+#define TEV_REACH_ROWS(BUF, BT)                                                                 \
+    {                                                                                           \
+        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
+            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
+            if (v < B) {                                                                        \
+                const bool ok = lane < nc;                                                      \
+                const float mc = ok ? pm[BUF][q] : -kInf;                                       \
+                const float M = wave::max_f32(mc);                                              \
+                const unsigned f = wave::or_u32(ok ? pf[BUF][q] : 0u);                          \
+                const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;                        \
+                const double incl = wave::incl_scan_f64(ok ? pr[BUF][q] * sc : 0.0, lane);      \
+                if (ok) W.rcum[(rb0 + v) * nc + lane] = incl;                                   \
+                finish_row(v, M, f, wave::last_lane_d(incl), ok ? pcs[BUF][q] * sc : 0.0);      \
+            }                                                                                   \
+        }                                                                                       \
+    }
+        static_assert(MAX_BATCHES == 4 && NB >= 1 && NB <= 4, "the pipeline below covers four batches");
+        if constexpr (NB > 1) TEV_REACH_LOAD(1, 1)
+        TEV_REACH_ROWS(0, 0)
+        if constexpr (NB > 2) TEV_REACH_LOAD(0, 2)
+        if constexpr (NB > 1) TEV_REACH_ROWS(1, 1)
+        if constexpr (NB > 3) TEV_REACH_LOAD(1, 3)
+        if constexpr (NB > 2) TEV_REACH_ROWS(0, 2)
+        if constexpr (NB > 3) TEV_REACH_ROWS(1, 3)
+#undef TEV_REACH_ROWS
+    } else {
+        for (int v = wave; v < B; v += REACH_WAVES) {
             const size_t base = (rb0 + v) * nc;
-            float M;
-            unsigned f;
+            float M = -kInf;
+            unsigned f = 0u;
+            for (int cc = lane; cc < nc; cc += 64) {
+                M = fmaxf(M, W.part_m[base + cc]);
+                f |= W.flags[base + cc];
+            }
+            M = wave::max_f32(M);
+            f = wave::or_u32(f);
             double carry = 0.0, csum = 0.0;
-            if (fast) {
-                M = wave::max_f32(fmaxf(pm[q][0], pm[q][1]));
-                f = wave::or_u32(pf[q][0] | pf[q][1]);
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const int cc = lane + 64 * h;
-                    const double sc = (pm[q][h] > -kInf) ? exp2((double)pm[q][h] - (double)M) : 0.0;
-                    const double rs = pr[q][h] * sc;
-                    csum += pcs[q][h] * sc;
-                    const double incl = wave::incl_scan_f64(rs, lane);
-                    if (cc < nc) W.rcum[base + cc] = carry + incl;
-                    carry += wave::last_lane_d(incl);
+            for (int b0 = 0; b0 < nc; b0 += 64) {
+                const int cc = b0 + lane;
+                double rs = 0.0;
+                if (cc < nc) {
+                    const float mc = W.part_m[base + cc];
+                    const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;
+                    rs = W.part_r[base + cc] * sc;
+                    csum += W.part_c[base + cc] * sc;
                 }
-            } else {
-                M = -kInf;
-                f = 0u;
-                for (int cc = lane; cc < nc; cc += 64) {
-                    M = fmaxf(M, W.part_m[base + cc]);
-                    f |= W.flags[base + cc];
-                }
-                M = wave::max_f32(M);
-                f = wave::or_u32(f);
-                for (int b0 = 0; b0 < nc; b0 += 64) {
-                    const int cc = b0 + lane;
-                    double rs = 0.0;
-                    if (cc < nc) {
-                        const float mc = W.part_m[base + cc];
-                        const double sc = (mc > -kInf) ? exp2((double)mc - (double)M) : 0.0;
-                        rs = W.part_r[base + cc] * sc;
-                        csum += W.part_c[base + cc] * sc;
-                    }
-                    const double incl = wave::incl_scan_f64(rs, lane);
-                    if (cc < nc) W.rcum[base + cc] = carry + incl;
-                    carry += wave::last_lane_d(incl);
-                }
+                const double incl = wave::incl_scan_f64(rs, lane);
+                if (cc < nc) W.rcum[base + cc] = carry + incl;
+                carry += wave::last_lane_d(incl);
             }
-            csum = wave::sum_f64(csum);
-            const double Z = carry + csum;
-            if (!(M > -kInf) || !(Z > 0.0) || isnan(Z)) f |= TEV_FLAG_NONFINITE;
-            if (lane == 0) {
-                s_M[v] = M;
-                s_Z[v] = Z;
-                s_rho[v] = carry / Z;
-                W.row_m[rb0 + v] = M;
-                if (f) atomicOr(&s_flags, f);
-            }
+            finish_row(v, M, f, carry, csum);
         }
+    }
+#undef TEV_REACH_LOAD
+    __syncthreads();
+
+    // Child probability of every node under its parent's distribution (fp64),
+    // kept as the node's initial path product.
+    // (the gathered logit is first touched here, so only this point waits for it)
+    asm volatile("" : "+v"(lraw));
+    const unsigned fl = s_flags;
+    if (fl == 0u && mine) {
+        double pc = 1.0;   // root: P(0) = 1
+        if (tid > 0)
+            pc = exp2((double)to_f32<T>(lraw) * (double)sL - (double)s_M[pa]) / s_Z[pa];
+        s_prod[tid] = pc;
     }
     __syncthreads();
     if (wave != 0) return;
 
     // ---- tree pass (wave 0): lane owns nodes NPL*lane .. NPL*lane + NPL - 1 ----
-    const unsigned fl = s_flags;
     if (fl) {
         const float qnan = __builtin_nanf("");
 #pragma unroll
@@ -334,46 +375,58 @@ __global__ __launch_bounds__(REACH_THREADS) void k_reach(
         }
         return;
     }
-    int pa[NPL], depth[NPL];
-    double pc[NPL];
-    int maxd = 0;
+    // Reach P(u) = product of child probabilities along u's root path (Eq. 4,
+    // evaluated level by level in Algorithm 1).  Here by pointer jumping:
+    // node u keeps (a, q) with P(u) = P(a) q; each round replaces (a, q) by
+    // (a's a, q times a's q), so a path of depth d is done after
+    // ceil(log2 d) rounds (a = 0 ends it, P(0) = 1).
+    int a[NPL];
+    double q[NPL];
 #pragma unroll
     for (int k = 0; k < NPL; k++) {
         const int u = lane * NPL + k;
-        pa[k] = 0;
-        depth[k] = 0;
-        pc[k] = 0.0;
-        if (u > 0 && u < B) {
-            pa[k] = s_par[u];
-            const int tk = tokens[rb0 + u];
-            const float l = to_f32<T>(logits[(rb0 + pa[k]) * (size_t)V + tk]);
-            pc[k] = exp2((double)l * (double)sL - (double)s_M[pa[k]]) / s_Z[pa[k]];
-            for (int j = u; j > 0; j = s_par[j]) depth[k]++;
-            maxd = max(maxd, depth[k]);
-        }
+        a[k] = (u > 0 && u < B) ? s_anc[u] : 0;
+        q[k] = (u < B) ? s_prod[u] : 0.0;
     }
-    maxd = wave::max_i32(maxd);
-    // Reach, level by level (Algorithm 1's loop over depth): the nodes of
-    // depth d read their parent's P, final since the previous level.
-    if (lane == 0) s_P[0] = 1.0;
-    for (int d = 1; d <= maxd; d++) {
-        wave::lds_sync();
+    bool open = false;
 #pragma unroll
-        for (int k = 0; k < NPL; k++)
-            if (depth[k] == d) s_P[lane * NPL + k] = s_P[pa[k]] * pc[k];
+    for (int k = 0; k < NPL; k++) open |= a[k] != 0;
+    while (__any(open)) {
+        int na[NPL];
+        double nq[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            na[k] = 0;
+            nq[k] = q[k];
+            if (a[k] != 0) {
+                na[k] = s_anc[a[k]];
+                nq[k] = q[k] * s_prod[a[k]];
+            }
+        }
+        wave::lds_sync();   // every read of this round precedes every write
+        open = false;
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            const int u = lane * NPL + k;
+            if (a[k] != 0) {
+                s_anc[u] = na[k];
+                s_prod[u] = nq[k];
+            }
+            a[k] = na[k];
+            q[k] = nq[k];
+            open |= a[k] != 0;
+        }
+        wave::lds_sync();
     }
-    wave::lds_sync();
-    double P[NPL], w[NPL];
+    double w[NPL];
     double lane_c = 0.0, lane_w = 0.0;
 #pragma unroll
     for (int k = 0; k < NPL; k++) {
         const int u = lane * NPL + k;
-        P[k] = 0.0;
         w[k] = 0.0;
         if (u < B) {
-            P[k] = s_P[u];
-            w[k] = P[k] * s_rho[u];
-            if (u > 0) lane_c += P[k];
+            w[k] = q[k] * s_rho[u];
+            if (u > 0) lane_c += q[k];
         }
     }
     const double C = wave::sum_f64(lane_c);
@@ -388,7 +441,7 @@ __global__ __launch_bounds__(REACH_THREADS) void k_reach(
         if (u < B) {
             W.wcum[rb0 + u] = run;
             rho_out[rb0 + u] = (float)s_rho[u];
-            reach_out[rb0 + u] = (float)P[k];
+            reach_out[rb0 + u] = (float)q[k];
             w_out[rb0 + u] = (float)w[k];
         }
     }
@@ -405,11 +458,9 @@ __global__ __launch_bounds__(REACH_THREADS) void k_reach(
 // child tokens are zero (bit j of the lane's mask word).
 // ----------------------------------------------------------------------------
 template <typename T, bool VEC>
-__device__ __forceinline__ void segment_terms(const T *chunk, int len, float sL, float Mc,
-                                              uint64_t bits, int lane, float *e) {
+__device__ __forceinline__ void segment_load(const T *chunk, int len, int lane, float *x) {
     constexpr int VW = 16 / (int)sizeof(T);
     const int base = lane * EPT;
-    float x[EPT];
 #pragma unroll
     for (int k = 0; k < EPT / VW; k++) {
         const int idx = base + k * VW;
@@ -425,9 +476,13 @@ __device__ __forceinline__ void segment_terms(const T *chunk, int len, float sL,
             for (int j = 0; j < VW; j++) x[k * VW + j] = (idx + j < len) ? to_f32<T>(chunk[idx + j]) : -kInf;
         }
     }
+}
+__device__ __forceinline__ void segment_terms(const float *x, float sL, float Mc, uint64_t bits,
+                                              float *e) {
+    const float off = (Mc > -kInf) ? Mc : 0.f;   // a chunk of -inf logits has only zero terms
 #pragma unroll
     for (int j = 0; j < EPT; j++) {
-        const float t = __builtin_amdgcn_exp2f(fmaf(x[j], sL, -Mc));
+        const float t = __builtin_amdgcn_exp2f(fmaf(x[j], sL, -off));
         e[j] = ((bits >> j) & 1ull) ? 0.f : t;
     }
 }
@@ -443,6 +498,25 @@ __device__ __forceinline__ uint64_t segment_child_bits(const int32_t *par, const
     for (int u = 1 + lane; u < B; u += 64) {
         if (par[u] == node) {
             const int o = tok[u] - c0;
+            if (o >= 0 && o < len) atomicOr(&s_wmask[o >> 5], 1u << (o & 31));
+        }
+    }
+    wave::lds_sync();
+    return (uint64_t)s_wmask[2 * lane] | ((uint64_t)s_wmask[2 * lane + 1] << 32);
+}
+
+// The same mask from parents/tokens already in registers: lane t holds nodes
+// 1 + t + 64k.
+__device__ __forceinline__ uint64_t child_bits_regs(const int (&cpar)[NPL], const int (&ctok)[NPL],
+                                                    int node, int c0, int len, unsigned *s_wmask,
+                                                    int lane) {
+    s_wmask[2 * lane] = 0u;
+    s_wmask[2 * lane + 1] = 0u;
+    wave::lds_sync();
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        if (cpar[k] == node) {
+            const int o = ctok[k] - c0;
             if (o >= 0 && o < len) atomicOr(&s_wmask[o >> 5], 1u << (o & 31));
         }
     }
@@ -468,18 +542,33 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_sample(
     __shared__ unsigned s_mask[WAVES_PER_WG][128];
     if (n >= n_draws) return;
     const size_t kd = (size_t)r * n_draws + n;
-    if (status[r] != 0u) {
+    // Loads in three rounds, each issued as one group: (1) everything that
+    // does not depend on the draw, (2) the exit node's running residual sums,
+    // (3) the one chunk that holds the bonus token.
+    const unsigned st = status[r];
+    const double u1 = (double)uniforms[2 * kd];
+    const double u2 = (double)uniforms[2 * kd + 1];
+    const double *Wc = wcum + (size_t)r * B;
+    const double Wtot = Wc[B - 1];
+    double wv[NPL];
+    int cpar[NPL], ctok[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        const int j = lane + 64 * k, u = 1 + j;
+        wv[k] = (j < B) ? Wc[j] : 0.0;
+        cpar[k] = (u < B) ? parents[(size_t)r * B + u] : -1;
+        ctok[k] = (u < B) ? tokens[(size_t)r * B + u] : 0;
+    }
+    if (st != 0u) {
         if (lane == 0) { exit_node[kd] = -1; bonus_token[kd] = -1; }
         return;
     }
-    const double u1 = (double)uniforms[2 * kd];
-    const double u2 = (double)uniforms[2 * kd + 1];
 
     // Exit node: the number of j with W_j <= u1 * S is the smallest j with u1 S < W_j.
-    const double *Wc = wcum + (size_t)r * B;
-    const double t1 = u1 * Wc[B - 1];
+    const double t1 = u1 * Wtot;
     int cnt = 0;
-    for (int j = lane; j < B; j += 64) cnt += (Wc[j] <= t1) ? 1 : 0;
+#pragma unroll
+    for (int k = 0; k < NPL; k++) cnt += (lane + 64 * k < B && wv[k] <= t1) ? 1 : 0;
     int Vn = wave::sum_i32(cnt);
     if (Vn >= B) {   // rounding left no bin: last node with positive mass
         int best = -1;
@@ -501,17 +590,19 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_sample(
             if (part_r[rb * nc + c] > 0.0) best = max(best, c);
         cc = max(wave::max_i32(best), 0);
     }
+    const int c0 = cc * CHUNK;
+    const int len = min(CHUNK, V - c0);
+    float x[EPT];
+    segment_load<T, VEC>(logits + rb * (size_t)V + c0, len, lane, x);
     const double before = (cc > 0) ? RC[cc - 1] : 0.0;
     const float Mv = row_m[rb];
     const float Mc = part_m[rb * nc + cc];
-    const double target = (t2 - before) * exp2((double)Mv - (double)Mc);
+    // offsets are integers with Mc <= Mv: the rescale is an exact power of two
+    const double target = __builtin_ldexp(t2 - before, (int)fminf(Mv - Mc, 2000.f));
 
-    const int c0 = cc * CHUNK;
-    const int len = min(CHUNK, V - c0);
-    const uint64_t bits = segment_child_bits(parents + (size_t)r * B, tokens + (size_t)r * B, B, Vn,
-                                             c0, len, s_mask[wave_id], lane);
+    const uint64_t bits = child_bits_regs(cpar, ctok, Vn, c0, len, s_mask[wave_id], lane);
     float e[EPT];
-    segment_terms<T, VEC>(logits + rb * (size_t)V + c0, len, sL, Mc, bits, lane, e);
+    segment_terms(x, sL, Mc, bits, e);
     double seg = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; j++) seg += (double)e[j];
@@ -558,11 +649,13 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_residual_cdf(
     const double before = (cc > 0) ? RC[cc - 1] : 0.0;
     const float Mv = row_m[rb];
     const float Mc = part_m[rb * nc + cc];
-    const double scale = exp2((double)Mc - (double)Mv);
+    const double scale = pow2_int(Mc - Mv);
+    float x[EPT];
+    segment_load<T, VEC>(logits + rb * (size_t)V + c0, len, lane, x);
     const uint64_t bits = segment_child_bits(parents + (size_t)r * B, tokens + (size_t)r * B, B, node,
                                              c0, len, s_mask[wave_id], lane);
     float e[EPT];
-    segment_terms<T, VEC>(logits + rb * (size_t)V + c0, len, sL, Mc, bits, lane, e);
+    segment_terms(x, sL, Mc, bits, e);
     double seg = 0.0;
 #pragma unroll
     for (int j = 0; j < EPT; j++) seg += (double)e[j];
@@ -597,8 +690,15 @@ hipError_t exit_law_impl(const T *logits, const int32_t *parents, const int32_t 
     const ExitPtrs P = exit_ptrs(ws, R, B, V);
     k_vocab<T, VEC><<<dim3((nc + WAVES_PER_WG - 1) / WAVES_PER_WG, R * B), VOCAB_THREADS, 0, st>>>(
         logits, parents, tokens, B, V, nc, sL, P);
-    k_reach<T><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho,
-                                                   reach, w, cov);
+    const int nb = (B + REACH_WAVES * ROW_BATCH - 1) / (REACH_WAVES * ROW_BATCH);
+    if (nb <= 1)
+        k_reach<T, 1><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
+    else if (nb == 2)
+        k_reach<T, 2><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
+    else if (nb == 3)
+        k_reach<T, 3><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
+    else
+        k_reach<T, 4><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
     return hipGetLastError();
 }
 
