@@ -3,7 +3,9 @@
 The library is built from the HIP sources in ``csrc/`` into
 ``draft_tree_verification_amd/_build/libtev.so``.  Packed fp32 vector ops are
 disabled for device code (``-packed-fp32-ops``); hipcc's host pass warns that it
-does not know the feature, which is harmless.
+does not know the feature, which is harmless.  MFMA accumulators are kept in
+ordinary VGPRs (``-amdgpu-mfma-vgpr-form``): the attention kernel fits its 256
+registers per wave that way, with no copies between register files.
 """
 from __future__ import annotations
 
@@ -24,6 +26,7 @@ def hipcc_command(out: str = LIB, extra: list[str] | None = None) -> list[str]:
     return ([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Wall", "-Wno-unused-function",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-o", out] + [os.path.join(CSRC, s) for s in SOURCES] + (extra or []))
 
 

@@ -6,20 +6,23 @@
 // (itself included) of kv head g = h / G, G = Hq / Hkv; cache row P + j holds
 // tree node j.
 //
-// k_attn_mfma (bf16): one workgroup serves up to NW*NQT*16 query rows of one
-// (request, kv head) -- the G*B rows (node i, head g*G + hh) share that head's
-// K/V, so the GQA group times the tree makes the products dense -- over one
-// split of the prefix; the last split also takes the B tree rows under the
-// ancestor mask.  Per 32-key block, K (row-major) and V (transposed, key pairs
-// packed in 32-bit words) are staged in LDS, double buffered, while the next
-// block's global loads are in flight.  Scores are formed transposed,
+// k_attn_mfma (bf16): one workgroup of eight waves serves up to 64 NQT query
+// rows of one (request, kv head) -- the G*B rows (node i, head g*G + hh) share
+// that head's K/V, so the GQA group times the tree makes the products dense --
+// over one split of the prefix; the last split also takes the B tree rows
+// under the ancestor mask.  Four waves take the rows of the block, two key
+// groups take alternate 32-key blocks of each 64-key stage (two waves per
+// SIMD), and the groups' results are merged through LDS at the end.  K and V
+// stages sit row-major in LDS, double buffered, while the next stages' global
+// loads are in flight.  Scores are formed transposed,
 //   S^T (32 keys x 16 queries) = K (32 x D) . Q^T (D x 16),
-// with v_mfma_f32_16x16x32_bf16, so each lane holds one query column; the
-// online-softmax probabilities of that column are exactly the B operand of
+// with v_mfma_f32_16x16x32_bf16, so each lane holds one query column; its
+// online-softmax probabilities, split into bf16 hi + lo parts, are exactly the
+// B operand of
 //   O^T (D x 16) += V^T (D x 32 keys) . P^T (32 keys x 16),
-// with the 32 keys of a block taken in the order the score tiles leave them
-// in registers (the V^T operand is read from LDS in the same order).  Tree
-// rows are masked by a per-node ancestor bitmap in LDS (one bit per node).
+// whose V^T operand comes straight from the row-major V stage through the
+// transposing LDS read, in the key order the score tiles leave in registers.
+// Tree rows are masked by a per-node ancestor bitmap in LDS (one bit per node).
 // Partial results of split prefixes are merged by k_attn_combine.
 //
 // k_attn_alu (fp32): one wave per query row, lanes over head_dim, online
@@ -40,13 +43,13 @@ namespace {
 constexpr float kInf = __builtin_inff();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Plain clang vectors for 16- and 8-byte moves: unlike HIP's u32x4 struct they
 // stay in registers (struct copies become memcpy that the compiler keeps in
 // memory).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 
 __device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
@@ -136,61 +139,62 @@ __global__ __launch_bounds__(256) void k_attn_alu(const float *__restrict__ q,
 // bf16 MFMA kernel.
 // ----------------------------------------------------------------------------
 constexpr int KB = 32;   // keys per block
-constexpr int kVsMin = -100;     // smallest V exponent shift (all-zero blocks)
 constexpr float kLazy = 8.0f;    // slack of the softmax reference max (log2 units)
 
-__device__ __forceinline__ uint32_t half_of(const u32x4 &x, int e) {
-    const uint32_t w = x[e >> 1];
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+constexpr int NW = 8;            // waves per workgroup: 4 row waves x 2 key groups
+constexpr int NT = NW * 64;
+constexpr int RWV = 4;           // row waves per key group
+constexpr int SB = 2 * KB;       // keys per stage: one block for each key group
+constexpr int PD = 2;            // stages in flight per workgroup (register prefetch depth)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane 4j + q fetches 8 bytes (four 16-bit values); lane i receives
+// value (i & 3) of the fetch of lane 4j + (i >> 2) in slot j, j = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-__device__ __forceinline__ f16x8 pack_f16x8(const float *p) {
-    f16x8 r;
+// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi): the product with bf16
+// V then carries about 16 significant bits of p.
+__device__ __forceinline__ void split_bf16x8(const float *p, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) r[e] = (_Float16)p[e];
-    return r;
+    for (int e = 0; e < 8; e++) {
+        const __bf16 h = (__bf16)p[e];
+        hi[e] = h;
+        lo[e] = (__bf16)(p[e] - (float)h);
+    }
 }
-
-// bf16 bit pattern -> fp16 bit pattern of the value times 2^-vs (exact while
-// the scaled magnitude stays within fp16's normal range).
-__device__ __forceinline__ uint32_t bf16_to_f16_scaled(uint32_t b, float scale) {
-    const float f = __uint_as_float(b << 16) * scale;
-    const _Float16 h = (_Float16)f;
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
-// Largest |value| of the 8 bf16 in x, as a 15-bit magnitude pattern (the
-// ordering of non-negative IEEE patterns is the ordering of the values).
-__device__ __forceinline__ uint32_t max_mag8(const u32x4 &x) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) m = max(m, max(x[i] & 0x7fffu, (x[i] >> 16) & 0x7fffu));
-    return m;
-}
-
-constexpr int PD = 4;   // K/V blocks in flight per workgroup (register prefetch depth)
 
 // Grid: a 1-D list of n_wg workgroup tasks (row block, prefix split, request *
 // kv head), row block fastest.  Hardware dispatches workgroup i to XCD i % 8,
 // so task L = (i % 8) * ceil(n_wg / 8) + i / 8 puts consecutive tasks -- the
 // row blocks that stream the same K/V -- on the same XCD and its L2.
-template <int D, int NQT, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_mfma(
+//
+// Waves: wave w serves query rows [(w & 3) * 16 NQT, +16 NQT) of the block
+// (NQT tiles of 16) over key group w >> 2, i.e. the 32-key block kg of every
+// 64-key stage; two waves per SIMD hide each other's latencies, and the two
+// groups' results are merged through LDS at the end.
+template <int D, int NQT>
+__global__ __launch_bounds__(NT) void k_attn_mfma(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const int32_t *__restrict__ parents, int B, int Hq, int Hkv,
     int P, float c_log2, int row_blocks, int splits, int keys_per_split, int n_wg,
     float *__restrict__ out, float *__restrict__ part_o, float *__restrict__ part_ml,
     unsigned *__restrict__ status) {
-    constexpr int NT = NW * 64;
     constexpr int DS = D / 32;          // k-steps of the score product
     constexpr int DT = D / 16;          // 16-row tiles of O^T
-    constexpr int KROW = D + 8;         // K row stride in LDS (bf16 elements)
-    constexpr int VROW = KB + 4;        // V^T row stride in LDS (fp16 elements)
-    constexpr int WR = NW * NQT * 16;   // query rows per workgroup
-    constexpr int K_ITEMS = KB * D / 8;         // 16-byte chunks of a K block
-    constexpr int V_ITEMS = (KB / 2) * (D / 8); // (key pair, 8-column) items of a V block
-    constexpr int NKI = (K_ITEMS + NT - 1) / NT;
-    constexpr int NVI = (V_ITEMS + NT - 1) / NT;
+    constexpr int RS = D + 8;           // K and V row stride in LDS (bf16 elements)
+    constexpr int WR = RWV * NQT * 16;  // query rows per workgroup
+    constexpr int ITEMS = SB * D / 8;   // 16-byte chunks of a stage's K (and of its V)
+    constexpr int NI = ITEMS / NT;
+    static_assert(ITEMS % NT == 0, "stage chunks must divide over the threads");
+    constexpr int STG = SB * RS;        // bf16 elements of one stage buffer of K (or V)
+    constexpr int STAGE_BYTES = 2 * 2 * STG * 2;
+    constexpr int XCH_BYTES = RWV * NQT * DT * 64 * 16;   // second group's accumulators
+    constexpr int SMEM = STAGE_BYTES > XCH_BYTES ? STAGE_BYTES : XCH_BYTES;
 
     const int per_xcd = (n_wg + 7) / 8;
     const int task = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
@@ -206,14 +210,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     __builtin_assume(tid < NT);
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
-    constexpr bool K_FULL = (K_ITEMS % NT) == 0;   // every thread owns NKI K chunks
-    constexpr bool V_FULL = (V_ITEMS % NT) == 0;
+    const int kg = wave >> 2, rw = wave & 3;
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KB * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * VROW];
+    // Stage buffers: K [2][SB][RS] then V [2][SB][RS], both row-major; after
+    // the loop the same bytes carry the second key group's accumulators.
+    __shared__ __attribute__((aligned(16))) unsigned char s_mem[SMEM];
+    uint16_t *const s_k = reinterpret_cast<uint16_t *>(s_mem);
+    uint16_t *const s_v = s_k + 2 * STG;
     __shared__ unsigned s_anc[TEV_MAX_NODES * 8];
     __shared__ int s_par[TEV_MAX_NODES];
-    __shared__ uint32_t s_wmax[2][NW];
+    __shared__ float s_xml[RWV][NQT][64][2];
     __shared__ int s_bad;
 
     const bool last = (sp == splits - 1);
@@ -222,76 +228,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int nkv = P + B;
     const uint16_t *kbase = k + ((size_t)r * Hkv + g) * (size_t)nkv * D;
     const uint16_t *vbase = v + ((size_t)r * Hkv + g) * (size_t)nkv * D;
-    const int nblocks = (kend - kbeg + KB - 1) / KB;
+    const int nstages = (kend - kbeg + SB - 1) / SB;
 
-    // PD register stages, one named array pair per stage
-    u32x4 kreg0[NKI], kreg1[NKI], kreg2[NKI], kreg3[NKI];
-    u32x4 vreg0[NVI][2], vreg1[NVI][2], vreg2[NVI][2], vreg3[NVI][2];
-    auto gload = [=](u32x4 (&kr)[NKI], u32x4 (&vr)[NVI][2], int kb) __attribute__((always_inline)) {
+    // PD register stages, one named array pair per stage; chunk n of a thread
+    // is (key, 8 columns) of both K and V, columns fastest (coalesced rows).
+    u32x4 kreg0[NI], kreg1[NI];
+    u32x4 vreg0[NI], vreg1[NI];
+    auto gload = [=](u32x4 (&kr)[NI], u32x4 (&vr)[NI], int kb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NKI; n++) {
+        for (int n = 0; n < NI; n++) {
             const int item = tid + n * NT;
-            if (K_FULL || item < K_ITEMS) {
-                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                const int kk = min(kb + key, nkv - 1);
-                kr[n] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)kk * D + d0);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NVI; n++) {
-            const int item = tid + n * NT;
-            if (V_FULL || item < V_ITEMS) {
-                const int kp = item % (KB / 2), d0 = (item / (KB / 2)) * 8;
-                const int k0 = min(kb + 2 * kp, nkv - 1), k1 = min(kb + 2 * kp + 1, nkv - 1);
-                vr[n][0] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)k0 * D + d0);
-                vr[n][1] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)k1 * D + d0);
-            } else {
-                vr[n][0] = u32x4{0u, 0u, 0u, 0u};
-                vr[n][1] = u32x4{0u, 0u, 0u, 0u};
-            }
+            const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
+            const size_t off = (size_t)min(kb + key, nkv - 1) * D + d0;
+            kr[n] = *reinterpret_cast<const u32x4 *>(kbase + off);
+            vr[n] = *reinterpret_cast<const u32x4 *>(vbase + off);
         }
     };
-    // Largest |V| of the block held in register slot sl, per wave, into s_wmax[buf].
-    auto publish_vmax = [=](const u32x4 (&vr)[NVI][2], uint32_t *wmax) __attribute__((always_inline)) {
-        uint32_t m = 0;
+    auto lstore = [=](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI], uint16_t *sk, uint16_t *sv)
+                      __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NVI; n++) m = max(m, max(max_mag8(vr[n][0]), max_mag8(vr[n][1])));
-        m = (uint32_t)wave::max_i32((int)m);
-        if (lane == 0) wmax[wave] = m;
-    };
-    // K as is; V transposed and converted to fp16 times 2^-vs.  vs is the
-    // smallest exponent seen so far that keeps every scaled |V| below 2^15: it
-    // only ever grows, so the accumulators change units only when a block with
-    // larger values arrives.
-    auto lstore = [=](const u32x4 (&kr)[NKI], const u32x4 (&vr)[NVI][2], uint16_t *sk, uint16_t *svt,
-                      const uint32_t *wmax, int &vs_run) __attribute__((always_inline)) {
-#pragma unroll
-        for (int n = 0; n < NKI; n++) {
+        for (int n = 0; n < NI; n++) {
             const int item = tid + n * NT;
-            if (K_FULL || item < K_ITEMS) {
-                const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
-                *reinterpret_cast<u32x4 *>(&sk[key * KROW + d0]) = kr[n];
-            }
-        }
-        uint32_t mb = 0;
-#pragma unroll
-        for (int w = 0; w < NW; w++) mb = max(mb, wmax[w]);
-        const int ebits = (int)(mb >> 7);                       // bf16 biased exponent
-        const int vs_need = mb == 0 ? kVsMin : min(max(ebits - 141, kVsMin), 15);
-        vs_run = max(vs_run, vs_need);
-        const float vscale = __builtin_ldexpf(1.0f, -vs_run);
-#pragma unroll
-        for (int n = 0; n < NVI; n++) {
-            const int item = tid + n * NT;
-            if (V_FULL || item < V_ITEMS) {
-                const int kp = item % (KB / 2), d0 = (item / (KB / 2)) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint32_t w = bf16_to_f16_scaled(half_of(vr[n][0], e), vscale) |
-                                       (bf16_to_f16_scaled(half_of(vr[n][1], e), vscale) << 16);
-                    *reinterpret_cast<uint32_t *>(&svt[(d0 + e) * VROW + 2 * kp]) = w;
-                }
-            }
+            const int key = item / (D / 8), d0 = (item % (D / 8)) * 8;
+            *reinterpret_cast<u32x4 *>(&sk[key * RS + d0]) = kr[n];
+            *reinterpret_cast<u32x4 *>(&sv[key * RS + d0]) = vr[n];
         }
     };
 
@@ -301,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     int qnode[NQT], qrow[NQT];
 #pragma unroll
     for (int t = 0; t < NQT; t++) {
-        const int row = rb * WR + wave * NQT * 16 + t * 16 + l16;
+        const int row = rb * WR + rw * NQT * 16 + t * 16 + l16;
         qrow[t] = row;
         const int rr = min(row, rows_total - 1);
         const int i = rr / G, hh = rr - i * G;
@@ -311,55 +271,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         for (int ds = 0; ds < DS; ds++)
             qop[t][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + ds * 32 + grp * 8));
     }
-    constexpr int NPAR = (TEV_MAX_NODES + NT - 1) / NT;
-    int my_par[NPAR];
-#pragma unroll
-    for (int n = 0; n < NPAR; n++) {
-        const int i = tid + n * NT;
-        my_par[n] = (last && i < B) ? parents[(size_t)r * B + i] : -1;
-    }
+    static_assert(NT >= TEV_MAX_NODES, "one thread per tree node");
+    const int my_par = (last && tid < B) ? parents[(size_t)r * B + tid] : -1;
 
-    if (0 < nblocks) gload(kreg0, vreg0, kbeg);
-    if (1 < nblocks) gload(kreg1, vreg1, kbeg + KB);
-    if (2 < nblocks) gload(kreg2, vreg2, kbeg + 2 * KB);
-    if (3 < nblocks) gload(kreg3, vreg3, kbeg + 3 * KB);
+    static_assert(PD == 2, "the pipeline below is written out for two register stages");
+    if (0 < nstages) gload(kreg0, vreg0, kbeg);
+    if (1 < nstages) gload(kreg1, vreg1, kbeg + SB);
 
     // Tree contract (parents[0] = -1, 0 <= parents[i] < i) and the ancestor
     // bitmap of every node (bit j of node i: j lies on i's root path).
     bool tree_ok = true;
     if (last) {
         if (tid == 0) s_bad = 0;
-#pragma unroll
-        for (int n = 0; n < NPAR; n++) {
-            const int i = tid + n * NT;
-            if (i < B) s_par[i] = my_par[n];
-        }
+        if (tid < B) s_par[tid] = my_par;
         __syncthreads();
-#pragma unroll
-        for (int n = 0; n < NPAR; n++) {
-            const int i = tid + n * NT, p = my_par[n];
-            if (i < B && !((i == 0) ? (p == -1) : (p >= 0 && p < i))) s_bad = 1;
-        }
+        if (tid < B && !((tid == 0) ? (my_par == -1) : (my_par >= 0 && my_par < tid))) s_bad = 1;
         __syncthreads();
         tree_ok = s_bad == 0;
-        if (tree_ok) {
+        if (tree_ok && tid < B) {
+            unsigned a[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            for (int j = tid; j >= 0; j = s_par[j]) {
 #pragma unroll
-            for (int n = 0; n < NPAR; n++) {
-                const int i = tid + n * NT;
-                if (i >= B) continue;
-                unsigned a[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-                for (int j = i; j >= 0; j = s_par[j]) {
-#pragma unroll
-                    for (int w = 0; w < 8; w++) a[w] |= ((j >> 5) == w) ? (1u << (j & 31)) : 0u;
-                }
-#pragma unroll
-                for (int w = 0; w < 8; w++) s_anc[i * 8 + w] = a[w];
+                for (int w = 0; w < 8; w++) a[w] |= ((j >> 5) == w) ? (1u << (j & 31)) : 0u;
             }
+#pragma unroll
+            for (int w = 0; w < 8; w++) s_anc[tid * 8 + w] = a[w];
         }
         if (rb == 0 && g == 0 && tid == 0) status[r] = tree_ok ? 0u : TEV_FLAG_TREE;
     }
 
-    f32x4 acc[NQT][DT];          // O^T in units of 2^-vs_cur
+    f32x4 acc[NQT][DT];          // O^T, un-normalised
     float m_run[NQT], l_run[NQT];
 #pragma unroll
     for (int t = 0; t < NQT; t++) {
@@ -368,15 +309,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    int vs_cur = kVsMin;   // unit of acc: 2^-vs_cur
-    int vs_run = kVsMin;   // unit of the V block last written to LDS
+    // This lane's fetch rows for the V^T operands: key 4 grp + (l16 >> 2) of
+    // each half-block, columns 4 (l16 & 3) of every 16-column tile.
+    const int vrow = 4 * grp + (l16 >> 2), vcol = 4 * (l16 & 3);
 
-    auto compute = [=](int kb, int buf, f32x4 (&acc)[NQT][DT], float (&m_run)[NQT], float (&l_run)[NQT],
-                       int &vs_cur, const int vs_blk) __attribute__((always_inline)) {
-        const float vfix = __builtin_ldexpf(1.0f, vs_cur - vs_blk);   // re-express acc in 2^-vs_blk
-        const bool vchange = vs_blk != vs_cur;
-        vs_cur = vs_blk;
+    // One 32-key block of this wave's key group: kb is its first key, buf the
+    // LDS stage buffer that holds it.
+    auto compute = [=](int kb, int buf, f32x4 (&acc)[NQT][DT], float (&m_run)[NQT], float (&l_run)[NQT])
+                       __attribute__((always_inline)) {
         const bool masked = (kb + KB > P) || (kb + KB > kend);
+        const uint16_t *sk = s_k + buf * STG + kg * KB * RS;
+        const uint16_t *sv = s_v + buf * STG + kg * KB * RS;
 
         // S^T tiles of every query tile: K operands loaded one key tile at a time.
         f32x4 S[NQT][2];
@@ -387,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
             bf16x8 kop[DS];
 #pragma unroll
             for (int ds = 0; ds < DS; ds++)
-                kop[ds] = *reinterpret_cast<const bf16x8 *>(&s_k[buf][(kt * 16 + l16) * KROW + ds * 32 + grp * 8]);
+                kop[ds] = *reinterpret_cast<const bf16x8 *>(&sk[(kt * 16 + l16) * RS + ds * 32 + grp * 8]);
 #pragma unroll
             for (int ds = 0; ds < DS; ds++)
 #pragma unroll
@@ -395,12 +338,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     S[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ds], qop[t][ds], S[t][kt], 0, 0, 0);
         }
 
-        // Online softmax per query column; P^T operands in fp16.
-        f16x8 pop[NQT];
+        // Online softmax per query column; P^T operands as bf16 hi + lo.
+        bf16x8 phi[NQT], plo[NQT];
 #pragma unroll
         for (int t = 0; t < NQT; t++) {
             // sv[e]: key kb + grp*4 + e (e < 4) or kb + 16 + grp*4 + (e - 4)
-            float sv[8] = {S[t][0][0], S[t][0][1], S[t][0][2], S[t][0][3],
+            float s8[8] = {S[t][0][0], S[t][0][1], S[t][0][2], S[t][0][3],
                            S[t][1][0], S[t][1][1], S[t][1][2], S[t][1][3]};
             if (masked) {
                 const unsigned *anc = &s_anc[qnode[t] * 8];
@@ -411,17 +354,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     const unsigned word = anc[(j >> 5) & 7];
                     const bool on_path = tree_ok & (j >= 0) & (((word >> (j & 31)) & 1u) != 0u);
                     const bool vis = (key < kend) & ((key < P) | on_path);
-                    sv[e] = vis ? sv[e] : -kInf;
+                    s8[e] = vis ? s8[e] : -kInf;
                 }
             }
-            float bm = sv[0];
+            float bm = s8[0];
 #pragma unroll
-            for (int e = 1; e < 8; e++) bm = fmaxf(bm, sv[e]);
+            for (int e = 1; e < 8; e++) bm = fmaxf(bm, s8[e]);
             bm = fmaxf(bm, __shfl_xor(bm, 16));
             bm = fmaxf(bm, __shfl_xor(bm, 32));
             // The reference max moves only when the block's max exceeds it by
-            // more than kLazy (log2 units): probabilities stay <= 2^kLazy, exact
-            // in fp16, and the accumulators are rescaled only when it moves.
+            // more than kLazy (log2 units): probabilities stay <= 2^kLazy and
+            // the accumulators are rescaled only when it moves.
             const float bmc = bm * c_log2;
             const bool grow = bmc > m_run[t] + kLazy;
             const float m_new = grow ? bmc : m_run[t];
@@ -431,67 +374,86 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
             float ps = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                pv[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c_log2, -m_use));
+                pv[e] = __builtin_amdgcn_exp2f(fmaf(s8[e], c_log2, -m_use));
                 ps += pv[e];
             }
             l_run[t] = l_run[t] * alpha + ps;
             m_run[t] = m_new;
-            if (vchange || __any(grow)) {
-                const float f = alpha * vfix;
+            if (__any(grow)) {
 #pragma unroll
-                for (int dt = 0; dt < DT; dt++) acc[t][dt] *= f;
+                for (int dt = 0; dt < DT; dt++) acc[t][dt] *= alpha;
             }
-            pop[t] = pack_f16x8(pv);
+            split_bf16x8(pv, phi[t], plo[t]);
         }
 
-        // O^T += V^T P^T: V operands loaded one d-tile at a time.
+        // O^T += V^T P^T: V^T operands by transposing reads, one d-tile at a time.
 #pragma unroll
         for (int dt = 0; dt < DT; dt++) {
-            const uint16_t *vr = &s_vt[buf][(dt * 16 + l16) * VROW];
-            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + grp * 4);
-            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 + grp * 4);
-            const f16x8 vop = __builtin_bit_cast(f16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            const i16x4 lo4 = lds_read_tr16(sv + vrow * RS + dt * 16 + vcol);
+            const i16x4 hi4 = lds_read_tr16(sv + (16 + vrow) * RS + dt * 16 + vcol);
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int t = 0; t < NQT; t++)
-                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[t], acc[t][dt], 0, 0, 0);
+            for (int t = 0; t < NQT; t++) {
+                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[t], acc[t][dt], 0, 0, 0);
+                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[t], acc[t][dt], 0, 0, 0);
+            }
         }
     };
 
-    // Block 0 into LDS buffer 0 (the tree bitmap above is also published here).
-    if (nblocks > 0) publish_vmax(vreg0, s_wmax[0]);
-    __syncthreads();
-    if (nblocks > 0) lstore(kreg0, vreg0, s_k[0], s_vt[0], s_wmax[0], vs_run);
+    // Stage 0 into LDS buffer 0 (the tree bitmap above is also published here).
+    if (nstages > 0) lstore(kreg0, vreg0, s_k, s_v);
     __syncthreads();
 
-    // Block b sits in register slot b % PD until it is written to LDS buffer
-    // b & 1 at the end of iteration b - 1; its slot is then refilled with block
-    // b + PD at the start of iteration b.
-    // One pipeline stage: block b = b0 + SL lives in stage SL's registers; NX is
-    // the stage that holds block b + 1.
+    // Stage s sits in register slot s % PD until it is written to LDS buffer
+    // s & 1 at the end of iteration s - 1; its slot is then refilled with
+    // stage s + PD at the start of iteration s.  SL is the slot of stage
+    // s = s0 + SL, NX the slot of stage s + 1.
 #define TEV_ATTN_STAGE(SL, NX)                                                                  \
     {                                                                                           \
-        const int b = b0 + (SL);                                                                \
-        if (b < nblocks) {                                                                      \
-            if (b + PD < nblocks) gload(kreg##SL, vreg##SL, kbeg + (b + PD) * KB);              \
-            compute(kbeg + b * KB, b & 1, acc, m_run, l_run, vs_cur, vs_run);                   \
-            if (b + 1 < nblocks) {                                                              \
-                const int nb = (b + 1) & 1;                                                     \
-                publish_vmax(vreg##NX, s_wmax[nb]);                                             \
+        const int s = s0 + (SL);                                                                \
+        if (s < nstages) {                                                                      \
+            if (s + PD < nstages) gload(kreg##SL, vreg##SL, kbeg + (s + PD) * SB);              \
+            const int kb = kbeg + s * SB + kg * KB;                                             \
+            if (kb < kend) compute(kb, s & 1, acc, m_run, l_run);                               \
+            if (s + 1 < nstages) {                                                              \
+                const int nb = (s + 1) & 1;                                                     \
                 __syncthreads(); /* all waves are done reading buffer nb */                     \
-                lstore(kreg##NX, vreg##NX, s_k[nb], s_vt[nb], s_wmax[nb], vs_run);              \
+                lstore(kreg##NX, vreg##NX, s_k + nb * STG, s_v + nb * STG);                     \
                 __syncthreads();                                                                \
             }                                                                                   \
         }                                                                                       \
     }
-    static_assert(PD == 4, "the pipeline below is written out for four register stages");
-    for (int b0 = 0; b0 < nblocks; b0 += PD) {
+    for (int s0 = 0; s0 < nstages; s0 += PD) {
         TEV_ATTN_STAGE(0, 1)
-        TEV_ATTN_STAGE(1, 2)
-        TEV_ATTN_STAGE(2, 3)
-        TEV_ATTN_STAGE(3, 0)
+        TEV_ATTN_STAGE(1, 0)
     }
 #undef TEV_ATTN_STAGE
-    const float vunscale = __builtin_ldexpf(1.0f, vs_cur);
+
+    // The second key group hands (m, l, acc) to the first through LDS.
+    __syncthreads();   // every wave is done with the stage buffers
+    f32x4 *xo = reinterpret_cast<f32x4 *>(s_mem);
+    if (kg == 1) {
+#pragma unroll
+        for (int t = 0; t < NQT; t++) {
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) xo[((rw * NQT + t) * DT + dt) * 64 + lane] = acc[t][dt];
+            s_xml[rw][t][lane][0] = m_run[t];
+            s_xml[rw][t][lane][1] = l_run[t];
+        }
+    }
+    __syncthreads();
+    if (kg == 1) return;   // no barrier below this point
+#pragma unroll
+    for (int t = 0; t < NQT; t++) {
+        const float m1 = s_xml[rw][t][lane][0], l1 = s_xml[rw][t][lane][1];
+        const float M = fmaxf(m_run[t], m1);
+        const float Mu = (M == -kInf) ? 0.f : M;
+        const float a0 = __builtin_amdgcn_exp2f(m_run[t] - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++) acc[t][dt] = acc[t][dt] * a0 + xo[((rw * NQT + t) * DT + dt) * 64 + lane] * a1;
+        l_run[t] = l_run[t] * a0 + l1 * a1;
+        m_run[t] = M;
+    }
 
     // Finalise: the four lanes of a query column hold disjoint key subsets.
     const size_t rows_all = (size_t)(n_wg / (row_blocks * splits)) * rows_total;
@@ -505,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int i = row / G, hh = row - i * G;
         if (splits == 1) {
             float *o = out + (((size_t)r * B + i) * Hq + g * G + hh) * D;
-            const float inv = vunscale / lt;
+            const float inv = 1.0f / lt;
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
                 f32x4 val = acc[t][dt] * inv;
@@ -516,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const size_t prow = (size_t)sp * rows_all + (size_t)rg * rows_total + row;
             float *o = part_o + prow * D;
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(o + dt * 16 + grp * 4) = acc[t][dt] * vunscale;
+            for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(o + dt * 16 + grp * 4) = acc[t][dt];
             if (grp == 0) {
                 part_ml[prow * 2] = m_run[t];
                 part_ml[prow * 2 + 1] = lt;
@@ -577,7 +539,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ 
     for (int j = 0; j < DPL; j++) dst[j] = bad ? __builtin_nanf("") : acc[j] / L;
 }
 
-template <int D, int NQT, int NW>
+template <int D, int NQT>
 hipError_t mfma_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      const int32_t *parents, int R, int B, int Hq, int Hkv, int P, float scale,
                      float *out, char *ws, const AttnPlan &pl, hipStream_t st) {
@@ -588,7 +550,7 @@ hipError_t mfma_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     unsigned *status = (unsigned *)(ws + L.status);
     const int n_wg = pl.row_blocks * pl.splits * R * Hkv;
     const int grid = 8 * ((n_wg + 7) / 8);
-    k_attn_mfma<D, NQT, NW><<<dim3(grid), NW * 64, 0, st>>>(
+    k_attn_mfma<D, NQT><<<dim3(grid), NT, 0, st>>>(
         q, k, v, parents, B, Hq, Hkv, P, c_log2, pl.row_blocks, pl.splits, pl.keys_per_split, n_wg,
         out, part_o, part_ml, status);
     if (pl.splits > 1) {
@@ -605,15 +567,18 @@ hipError_t mfma_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P) {
     (void)D;
     AttnPlan p{};
-    p.nqt = 2;
-    p.nw = 4;
-    p.rows_per_wg = p.nw * p.nqt * 16;
     const int G = Hq / Hkv;
-    p.row_blocks = (G * B + p.rows_per_wg - 1) / p.rows_per_wg;
+    const int rows = G * B;
+    // Query tiles per wave: as many as the rows fill (a workgroup serves
+    // 4 * 16 * nqt rows; two key groups share them).
+    p.nqt = rows > 64 ? 2 : 1;
+    p.nw = NW;
+    p.rows_per_wg = RWV * p.nqt * 16;
+    p.row_blocks = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
     const long base = (long)R * Hkv * p.row_blocks;
-    // Enough workgroups to cover 256 CUs twice, each split keeping >= 256
-    // prefix keys so that per-split fixed costs stay small.
-    long want = (512 + base - 1) / base;
+    // One workgroup per CU (256 CUs), each split keeping >= 256 prefix keys
+    // so that per-split fixed costs stay small.
+    long want = (256 + base - 1) / base;
     long maxs = P / 256;
     if (maxs < 1) maxs = 1;
     if (maxs > MAX_SPLITS) maxs = MAX_SPLITS;
@@ -622,7 +587,7 @@ AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P) {
     int kps = 0;
     if (S > 1) {
         kps = (P + S - 1) / S;
-        kps = (kps + KB - 1) / KB * KB;
+        kps = (kps + SB - 1) / SB * SB;
         S = (P + kps - 1) / kps;
     }
     p.splits = S;
@@ -646,8 +611,12 @@ hipError_t launch_tree_attn(const void *q, const void *k, const void *v, int dty
     }
     const AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P);
     const uint16_t *qb = (const uint16_t *)q, *kb = (const uint16_t *)k, *vb = (const uint16_t *)v;
-    if (D == 64) return mfma_impl<64, 2, 4>(qb, kb, vb, parents, R, B, Hq, Hkv, P, scale, out, ws, pl, st);
-    return mfma_impl<128, 2, 4>(qb, kb, vb, parents, R, B, Hq, Hkv, P, scale, out, ws, pl, st);
+#define TEV_ATTN_CASE(DD, QQ) \
+    if (D == DD && pl.nqt == QQ) return mfma_impl<DD, QQ>(qb, kb, vb, parents, R, B, Hq, Hkv, P, scale, out, ws, pl, st);
+    TEV_ATTN_CASE(64, 1) TEV_ATTN_CASE(64, 2)
+    TEV_ATTN_CASE(128, 1) TEV_ATTN_CASE(128, 2)
+#undef TEV_ATTN_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace tev
