@@ -2,17 +2,19 @@
 """Benchmark of one verification round on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-ancestor-masked tree attention for one layer (tev_tree_attn), the exit law
-(tev_exit_law) and TEV's exit-node and bonus-token draws with one uniform pair
-per request (tev_sample).  The default workload is the Qwen3-4B-shaped round:
+ancestor-masked tree attention for one layer, the exit law and TEV's exit-node
+and bonus-token draws with one uniform pair per request -- one call of
+tev_verify_round (or, with --separate, tev_tree_attn + tev_exit_law +
+tev_sample).  The default workload is the Qwen3-4B-shaped round:
 1 request, B = 64 tree nodes (root included), V = 151936 bf16 logits, 32/8
 heads of dim 128 over a 4096-token KV prefix.
 
 Timing: each step's three calls are captured in a HIP graph per input copy;
 the copies form a ring larger than the 256 MB Infinity Cache, so every step
 reads its inputs from HBM.  The timed region is bracketed by a device
-synchronisation and HIP events on the stream the kernels run on.  Per-call
-durations come from HIP events around graph replays of each call alone.
+synchronisation and HIP events on the stream the graphs are launched on.
+Per-call durations come from HIP events around graph replays of each call
+alone.
 
 The CPU baseline is the fp64 oracle timed on this host's cores on whole
 rounds of the same workload (bounded to about 10 s of CPU work).
@@ -113,6 +115,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--call-iters", type=int, default=100)
+    ap.add_argument("--separate", action="store_true",
+                    help="time the three calls tev_tree_attn, tev_exit_law, tev_sample instead of tev_verify_round")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -165,10 +169,21 @@ def main():
     def call_sample(s):
         tev.tev_sample(s["lg"], s["par"], s["tok"], ws_e, s["uni"], wl.inv_temperature, out=draws)
 
-    def step(s):
+    def step_separate(s):
         call_attn(s)
         call_exit(s)
         call_sample(s)
+
+    ws_r = torch.zeros(tev.tev_verify_round_workspace_bytes(R, B, V, wl.Hq, wl.Hkv, wl.D, wl.P),
+                       dtype=torch.uint8, device="cuda")
+    round_out = tev.RoundResult(out_attn, el_out.rho, el_out.reach, el_out.exit_mass, el_out.coverage,
+                                draws[0], draws[1], ws_r)
+
+    def step_round(s):
+        tev.tev_verify_round(s["q"], s["k"], s["v"], s["lg"], s["par"], s["tok"], s["uni"], wl.P,
+                             wl.scale, wl.inv_temperature, out=round_out)
+
+    step = step_separate if args.separate else step_round
 
     # eager check of one round before capture
     step(slots[0])
@@ -277,7 +292,9 @@ def main():
         "data": "synthetic (seeded; shapes of the pages' Qwen3 workloads)",
         "config": {"workload": wl.name, "requests": R, "nodes_per_request": B, "vocab": V,
                    "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D, "kv_prefix": wl.P,
-                   "draws_per_request": 1, "ring_copies": ring, "graph": True},
+                   "draws_per_request": 1, "ring_copies": ring, "graph": True,
+                   "call": "tev_tree_attn + tev_exit_law + tev_sample" if args.separate
+                   else "tev_verify_round"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

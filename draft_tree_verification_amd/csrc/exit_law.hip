@@ -39,45 +39,12 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "exit_law_dev.h"
 #include "tev_internal.h"
 #include "wave_ops.h"
 
 namespace tev {
 namespace {
-
-constexpr float kInf = __builtin_inff();
-constexpr int NPL = TEV_MAX_NODES / 64;   // tree nodes per lane in the tree pass
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <typename T>
-__device__ __forceinline__ float to_f32(T x);
-template <>
-__device__ __forceinline__ float to_f32<float>(float x) { return x; }
-template <>
-__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
-    return __uint_as_float(((uint32_t)x) << 16);
-}
-
-// 16 bytes of logits -> floats.
-__device__ __forceinline__ void load16(const float *p, float *x) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-__device__ __forceinline__ void load16(const uint16_t *p, float *x) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(p);
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-}
-
-struct ExitPtrs {
-    unsigned *status, *flags;
-    float *part_m, *row_m;
-    double *part_r, *part_c, *rcum, *wcum;
-};
 
 // ----------------------------------------------------------------------------
 // k_vocab.  Chunk c of row rv: lane t holds the elements k*(64*VW) + t*VW + j
@@ -125,12 +92,17 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
     s_mask[wave][2 * lane + 1] = 0u;
     wave::lds_sync();
     bool dup = false;
-    for (int u = 1 + lane; u < B; u += 64) {
-        if (par[u] == v) {
+    int mine_o[NPL];   // chunk offset of child 1 + lane + 64 k, or -1
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        mine_o[k] = -1;
+        const int u = 1 + lane + 64 * k;
+        if (u < B && par[u] == v) {
             const int o = tok[u] - c0;
             if (o >= 0 && o < len) {
-                const int k = o / SPAN, rem = o - k * SPAN;
-                const int bitpos = k * VW + (rem % VW);            // 0..63 within the owner lane
+                mine_o[k] = o;
+                const int kk = o / SPAN, rem = o - kk * SPAN;
+                const int bitpos = kk * VW + (rem % VW);           // 0..63 within the owner lane
                 const unsigned bit = 1u << (bitpos & 31);
                 const unsigned old = atomicOr(&s_mask[wave][2 * (rem / VW) + (bitpos >> 5)], bit);
                 dup |= (old & bit) != 0u;
@@ -199,427 +171,31 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
         W.part_r[o] = Rc;
         W.part_c[o] = Cc;
     }
+    // Each child token of v lies in exactly one chunk of v's row: that chunk
+    // records the child's own term (the same f32 operations as the sums) and
+    // the chunk offset, so the reach needs no gather of its own.
+    if (wave_has_children) {
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            if (mine_o[k] >= 0) {
+                const float xl = to_f32<T>(row[mine_o[k]]);
+                const float t = (m > -kInf) ? __builtin_amdgcn_exp2f(fmaf(xl, sL, -Mc)) : 0.f;
+                W.cterm[(size_t)r * B + 1 + lane + 64 * k] = make_float2(t, Mc);
+            }
+        }
+    }
 }
 
-// ----------------------------------------------------------------------------
-// k_reach.
-// ----------------------------------------------------------------------------
 constexpr int REACH_THREADS = 1024;
-constexpr int REACH_WAVES = REACH_THREADS / 64;
-constexpr int ROW_BATCH = 4;        // rows per wave whose partials are loaded together
-constexpr int FAST_NC = 64;         // chunks per row held in registers (one per lane)
-constexpr int MAX_BATCHES = (TEV_MAX_NODES + REACH_WAVES * ROW_BATCH - 1) / (REACH_WAVES * ROW_BATCH);
 
-// 2^e for an integer-valued e <= 0 (chunk offsets are integers): exact.
-__device__ __forceinline__ double pow2_int(float e) {
-    return __builtin_ldexp(1.0, (int)fmaxf(e, -2000.f));
+template <int NB>
+__global__ __launch_bounds__(REACH_THREADS) void k_reach(ReachArgs a) {
+    reach_wg<NB, REACH_THREADS>(a, (int)blockIdx.x);
 }
 
-// NB = ceil(B / (REACH_WAVES * ROW_BATCH)) batches, a template parameter so
-// that every load of the pipeline is unconditional.
-template <typename T, int NB>
-__global__ __launch_bounds__(REACH_THREADS) void k_reach(
-    const T *__restrict__ logits, const int32_t *__restrict__ parents,
-    const int32_t *__restrict__ tokens, int B, int V, int nc, float sL, ExitPtrs W,
-    float *__restrict__ rho_out, float *__restrict__ reach_out, float *__restrict__ w_out,
-    float *__restrict__ cov_out) {
-    const int r = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    __shared__ int s_anc[TEV_MAX_NODES];
-    __shared__ float s_M[TEV_MAX_NODES];
-    __shared__ double s_Z[TEV_MAX_NODES];
-    __shared__ double s_rho[TEV_MAX_NODES];
-    __shared__ double s_prod[TEV_MAX_NODES];
-    __shared__ unsigned s_flags;
-    const size_t rb0 = (size_t)r * B;
-    const bool fast = nc <= FAST_NC;
-
-    // Issue order: the tree arrays, then this wave's first batch of chunk
-    // partials, then (once parents and tokens are in) the child-logit
-    // gathers; no global store is issued before the last load.
-    // Every load below is unconditional (out-of-range lanes read a clamped,
-    // valid address and discard the value): conditional loads would make the
-    // compiler wait for all outstanding loads where the branches join.
-    const bool mine = tid < B;
-    const int ti = min(tid, B - 1);
-    const int pa = parents[rb0 + ti];
-    const int tk = tokens[rb0 + ti];
-    float pm[2][ROW_BATCH];
-    unsigned pf[2][ROW_BATCH];
-    double pr[2][ROW_BATCH], pcs[2][ROW_BATCH];
-    // Loads the partials of batch BT (rows wave + REACH_WAVES * (ROW_BATCH * BT + q)) into buffer BUF.
-#define TEV_REACH_LOAD(BUF, BT)                                                                 \
-    {                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
-            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
-            const bool ok = v < B && lane < nc;   /* masked where used; unused when !fast */   \
-            const size_t o = (rb0 + (ok ? v : 0)) * nc + (ok ? lane : 0);                       \
-            pm[BUF][q] = W.part_m[o];                                                           \
-            pf[BUF][q] = W.flags[o];                                                            \
-            pr[BUF][q] = W.part_r[o];                                                           \
-            pcs[BUF][q] = W.part_c[o];                                                          \
-        }                                                                                       \
-    }
-    TEV_REACH_LOAD(0, 0)
-    const bool bad = mine && ((tid == 0) ? (pa != -1) : (pa < 0 || pa >= tid || tk < 0 || tk >= V));
-    const bool child = mine && tid > 0 && !bad;
-    T lraw = logits[(rb0 + (child ? pa : 0)) * (size_t)V + (child ? tk : 0)];
-    if (tid == 0) s_flags = 0u;
-    __syncthreads();
-    if (mine) s_anc[tid] = child ? pa : 0;
-    if (bad) atomicOr(&s_flags, TEV_FLAG_TREE);
-
-    // ---- row pass: per row the fp64 combine of its chunk partials ----
-    // chunk offsets are integers, so rescaling a partial to the row offset M
-    // is an exact power of two.
-    auto finish_row = [&](int v, float M, unsigned f, double carry, double csum) {
-        csum = wave::sum_f64(csum);
-        const double Z = carry + csum;
-        if (!(M > -kInf) || !(Z > 0.0) || isnan(Z)) f |= TEV_FLAG_NONFINITE;
-        if (lane == 0) {
-            s_M[v] = M;
-            s_Z[v] = Z;
-            s_rho[v] = carry / Z;
-            W.row_m[rb0 + v] = M;
-            if (f) atomicOr(&s_flags, f);
-        }
-    };
-    if (fast) {
-#define TEV_REACH_ROWS(BUF, BT)                                                                 \
-    {                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
-            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
-            if (v < B) {                                                                        \
-                const bool ok = lane < nc;                                                      \
-                const float mc = ok ? pm[BUF][q] : -kInf;                                       \
-                const float M = wave::max_f32(mc);                                              \
-                const unsigned f = wave::or_u32(ok ? pf[BUF][q] : 0u);                          \
-                const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;                        \
-                const double incl = wave::incl_scan_f64(ok ? pr[BUF][q] * sc : 0.0, lane);      \
-                if (ok) W.rcum[(rb0 + v) * nc + lane] = incl;                                   \
-                finish_row(v, M, f, wave::last_lane_d(incl), ok ? pcs[BUF][q] * sc : 0.0);      \
-            }                                                                                   \
-        }                                                                                       \
-    }
-        static_assert(MAX_BATCHES == 4 && NB >= 1 && NB <= 4, "the pipeline below covers four batches");
-        if constexpr (NB > 1) TEV_REACH_LOAD(1, 1)
-        TEV_REACH_ROWS(0, 0)
-        if constexpr (NB > 2) TEV_REACH_LOAD(0, 2)
-        if constexpr (NB > 1) TEV_REACH_ROWS(1, 1)
-        if constexpr (NB > 3) TEV_REACH_LOAD(1, 3)
-        if constexpr (NB > 2) TEV_REACH_ROWS(0, 2)
-        if constexpr (NB > 3) TEV_REACH_ROWS(1, 3)
-#undef TEV_REACH_ROWS
-    } else {
-        for (int v = wave; v < B; v += REACH_WAVES) {
-            const size_t base = (rb0 + v) * nc;
-            float M = -kInf;
-            unsigned f = 0u;
-            for (int cc = lane; cc < nc; cc += 64) {
-                M = fmaxf(M, W.part_m[base + cc]);
-                f |= W.flags[base + cc];
-            }
-            M = wave::max_f32(M);
-            f = wave::or_u32(f);
-            double carry = 0.0, csum = 0.0;
-            for (int b0 = 0; b0 < nc; b0 += 64) {
-                const int cc = b0 + lane;
-                double rs = 0.0;
-                if (cc < nc) {
-                    const float mc = W.part_m[base + cc];
-                    const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;
-                    rs = W.part_r[base + cc] * sc;
-                    csum += W.part_c[base + cc] * sc;
-                }
-                const double incl = wave::incl_scan_f64(rs, lane);
-                if (cc < nc) W.rcum[base + cc] = carry + incl;
-                carry += wave::last_lane_d(incl);
-            }
-            finish_row(v, M, f, carry, csum);
-        }
-    }
-#undef TEV_REACH_LOAD
-    __syncthreads();
-
-    // Child probability of every node under its parent's distribution (fp64),
-    // kept as the node's initial path product.
-    // (the gathered logit is first touched here, so only this point waits for it)
-    asm volatile("" : "+v"(lraw));
-    const unsigned fl = s_flags;
-    if (fl == 0u && mine) {
-        double pc = 1.0;   // root: P(0) = 1
-        if (tid > 0)
-            pc = exp2((double)to_f32<T>(lraw) * (double)sL - (double)s_M[pa]) / s_Z[pa];
-        s_prod[tid] = pc;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-
-    // ---- tree pass (wave 0): lane owns nodes NPL*lane .. NPL*lane + NPL - 1 ----
-    if (fl) {
-        const float qnan = __builtin_nanf("");
-#pragma unroll
-        for (int k = 0; k < NPL; k++) {
-            const int u = lane * NPL + k;
-            if (u < B) {
-                rho_out[rb0 + u] = qnan;
-                reach_out[rb0 + u] = qnan;
-                w_out[rb0 + u] = qnan;
-                W.wcum[rb0 + u] = __builtin_nan("");
-            }
-        }
-        if (lane == 0) {
-            cov_out[r] = qnan;
-            W.status[r] = fl;
-        }
-        return;
-    }
-    // Reach P(u) = product of child probabilities along u's root path (Eq. 4,
-    // evaluated level by level in Algorithm 1).  Here by pointer jumping:
-    // node u keeps (a, q) with P(u) = P(a) q; each round replaces (a, q) by
-    // (a's a, q times a's q), so a path of depth d is done after
-    // ceil(log2 d) rounds (a = 0 ends it, P(0) = 1).
-    int a[NPL];
-    double q[NPL];
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        const int u = lane * NPL + k;
-        a[k] = (u > 0 && u < B) ? s_anc[u] : 0;
-        q[k] = (u < B) ? s_prod[u] : 0.0;
-    }
-    bool open = false;
-#pragma unroll
-    for (int k = 0; k < NPL; k++) open |= a[k] != 0;
-    while (__any(open)) {
-        int na[NPL];
-        double nq[NPL];
-#pragma unroll
-        for (int k = 0; k < NPL; k++) {
-            na[k] = 0;
-            nq[k] = q[k];
-            if (a[k] != 0) {
-                na[k] = s_anc[a[k]];
-                nq[k] = q[k] * s_prod[a[k]];
-            }
-        }
-        wave::lds_sync();   // every read of this round precedes every write
-        open = false;
-#pragma unroll
-        for (int k = 0; k < NPL; k++) {
-            const int u = lane * NPL + k;
-            if (a[k] != 0) {
-                s_anc[u] = na[k];
-                s_prod[u] = nq[k];
-            }
-            a[k] = na[k];
-            q[k] = nq[k];
-            open |= a[k] != 0;
-        }
-        wave::lds_sync();
-    }
-    double w[NPL];
-    double lane_c = 0.0, lane_w = 0.0;
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        const int u = lane * NPL + k;
-        w[k] = 0.0;
-        if (u < B) {
-            w[k] = q[k] * s_rho[u];
-            if (u > 0) lane_c += q[k];
-        }
-    }
-    const double C = wave::sum_f64(lane_c);
-    // Exit CDF: running sums in node order (lane-local, then across lanes).
-#pragma unroll
-    for (int k = 0; k < NPL; k++) lane_w += w[k];
-    double run = wave::incl_scan_f64(lane_w, lane) - lane_w;
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        const int u = lane * NPL + k;
-        run += w[k];
-        if (u < B) {
-            W.wcum[rb0 + u] = run;
-            rho_out[rb0 + u] = (float)s_rho[u];
-            reach_out[rb0 + u] = (float)q[k];
-            w_out[rb0 + u] = (float)w[k];
-        }
-    }
-    if (lane == 0) {
-        cov_out[r] = (float)C;
-        W.status[r] = 0u;
-    }
-}
-
-// ----------------------------------------------------------------------------
-// In-chunk residual terms on a contiguous segment: lane t owns tokens
-// [64t, 64t + 64) of the chunk, so a wave scan runs in token order.  Each term
-// is computed exactly as in the chunk pass (same f32 operations and offset);
-// child tokens are zero (bit j of the lane's mask word).
-// ----------------------------------------------------------------------------
 template <typename T, bool VEC>
-__device__ __forceinline__ void segment_load(const T *chunk, int len, int lane, float *x) {
-    constexpr int VW = 16 / (int)sizeof(T);
-    const int base = lane * EPT;
-#pragma unroll
-    for (int k = 0; k < EPT / VW; k++) {
-        const int idx = base + k * VW;
-        if (VEC) {
-            if (idx < len) {
-                load16(chunk + idx, &x[k * VW]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < VW; j++) x[k * VW + j] = -kInf;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx + j < len) ? to_f32<T>(chunk[idx + j]) : -kInf;
-        }
-    }
-}
-__device__ __forceinline__ void segment_terms(const float *x, float sL, float Mc, uint64_t bits,
-                                              float *e) {
-    const float off = (Mc > -kInf) ? Mc : 0.f;   // a chunk of -inf logits has only zero terms
-#pragma unroll
-    for (int j = 0; j < EPT; j++) {
-        const float t = __builtin_amdgcn_exp2f(fmaf(x[j], sL, -off));
-        e[j] = ((bits >> j) & 1ull) ? 0.f : t;
-    }
-}
-
-// Child tokens of `node` inside [c0, c0 + len) -> bit (o % 64) of lane
-// (o / 64)'s 64-bit mask, matching the contiguous ownership of segment_terms.
-__device__ __forceinline__ uint64_t segment_child_bits(const int32_t *par, const int32_t *tok, int B,
-                                                       int node, int c0, int len, unsigned *s_wmask,
-                                                       int lane) {
-    s_wmask[2 * lane] = 0u;
-    s_wmask[2 * lane + 1] = 0u;
-    wave::lds_sync();
-    for (int u = 1 + lane; u < B; u += 64) {
-        if (par[u] == node) {
-            const int o = tok[u] - c0;
-            if (o >= 0 && o < len) atomicOr(&s_wmask[o >> 5], 1u << (o & 31));
-        }
-    }
-    wave::lds_sync();
-    return (uint64_t)s_wmask[2 * lane] | ((uint64_t)s_wmask[2 * lane + 1] << 32);
-}
-
-// The same mask from parents/tokens already in registers: lane t holds nodes
-// 1 + t + 64k.
-__device__ __forceinline__ uint64_t child_bits_regs(const int (&cpar)[NPL], const int (&ctok)[NPL],
-                                                    int node, int c0, int len, unsigned *s_wmask,
-                                                    int lane) {
-    s_wmask[2 * lane] = 0u;
-    s_wmask[2 * lane + 1] = 0u;
-    wave::lds_sync();
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        if (cpar[k] == node) {
-            const int o = ctok[k] - c0;
-            if (o >= 0 && o < len) atomicOr(&s_wmask[o >> 5], 1u << (o & 31));
-        }
-    }
-    wave::lds_sync();
-    return (uint64_t)s_wmask[2 * lane] | ((uint64_t)s_wmask[2 * lane + 1] << 32);
-}
-
-// ----------------------------------------------------------------------------
-// k_sample: grid (ceil(n_draws / 4), R), 256 threads, one wave per draw.
-// ----------------------------------------------------------------------------
-template <typename T, bool VEC>
-__global__ __launch_bounds__(VOCAB_THREADS) void k_sample(
-    const T *__restrict__ logits, const int32_t *__restrict__ parents,
-    const int32_t *__restrict__ tokens, int B, int V, int nc, float sL,
-    const unsigned *__restrict__ status, const float *__restrict__ part_m,
-    const double *__restrict__ part_r, const float *__restrict__ row_m,
-    const double *__restrict__ rcum, const double *__restrict__ wcum,
-    const float *__restrict__ uniforms, int n_draws, int32_t *__restrict__ exit_node,
-    int32_t *__restrict__ bonus_token) {
-    const int wave_id = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = blockIdx.x * WAVES_PER_WG + wave_id;
-    const int r = blockIdx.y;
-    __shared__ unsigned s_mask[WAVES_PER_WG][128];
-    if (n >= n_draws) return;
-    const size_t kd = (size_t)r * n_draws + n;
-    // Loads in three rounds, each issued as one group: (1) everything that
-    // does not depend on the draw, (2) the exit node's running residual sums,
-    // (3) the one chunk that holds the bonus token.
-    const unsigned st = status[r];
-    const double u1 = (double)uniforms[2 * kd];
-    const double u2 = (double)uniforms[2 * kd + 1];
-    const double *Wc = wcum + (size_t)r * B;
-    const double Wtot = Wc[B - 1];
-    double wv[NPL];
-    int cpar[NPL], ctok[NPL];
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        const int j = lane + 64 * k, u = 1 + j;
-        wv[k] = (j < B) ? Wc[j] : 0.0;
-        cpar[k] = (u < B) ? parents[(size_t)r * B + u] : -1;
-        ctok[k] = (u < B) ? tokens[(size_t)r * B + u] : 0;
-    }
-    if (st != 0u) {
-        if (lane == 0) { exit_node[kd] = -1; bonus_token[kd] = -1; }
-        return;
-    }
-
-    // Exit node: the number of j with W_j <= u1 * S is the smallest j with u1 S < W_j.
-    const double t1 = u1 * Wtot;
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < NPL; k++) cnt += (lane + 64 * k < B && wv[k] <= t1) ? 1 : 0;
-    int Vn = wave::sum_i32(cnt);
-    if (Vn >= B) {   // rounding left no bin: last node with positive mass
-        int best = -1;
-        for (int j = lane; j < B; j += 64)
-            if (j == 0 ? (Wc[0] > 0.0) : (Wc[j] > Wc[j - 1])) best = max(best, j);
-        Vn = max(wave::max_i32(best), 0);
-    }
-
-    // Bonus token: the chunk whose running residual sum first exceeds u2 * T.
-    const size_t rb = (size_t)r * B + Vn;
-    const double *RC = rcum + rb * nc;
-    const double t2 = u2 * RC[nc - 1];
-    int cc = 0;
-    for (int c = lane; c < nc; c += 64) cc += (RC[c] <= t2) ? 1 : 0;
-    cc = wave::sum_i32(cc);
-    if (cc >= nc) {
-        int best = -1;
-        for (int c = lane; c < nc; c += 64)
-            if (part_r[rb * nc + c] > 0.0) best = max(best, c);
-        cc = max(wave::max_i32(best), 0);
-    }
-    const int c0 = cc * CHUNK;
-    const int len = min(CHUNK, V - c0);
-    float x[EPT];
-    segment_load<T, VEC>(logits + rb * (size_t)V + c0, len, lane, x);
-    const double before = (cc > 0) ? RC[cc - 1] : 0.0;
-    const float Mv = row_m[rb];
-    const float Mc = part_m[rb * nc + cc];
-    // offsets are integers with Mc <= Mv: the rescale is an exact power of two
-    const double target = __builtin_ldexp(t2 - before, (int)fminf(Mv - Mc, 2000.f));
-
-    const uint64_t bits = child_bits_regs(cpar, ctok, Vn, c0, len, s_mask[wave_id], lane);
-    float e[EPT];
-    segment_terms(x, sL, Mc, bits, e);
-    double seg = 0.0;
-#pragma unroll
-    for (int j = 0; j < EPT; j++) seg += (double)e[j];
-    double run = wave::incl_scan_f64(seg, lane) - seg;
-    int below = 0, last_pos = -1;
-#pragma unroll
-    for (int j = 0; j < EPT; j++) {
-        run += (double)e[j];
-        below += (run <= target) ? 1 : 0;
-        if (e[j] > 0.f) last_pos = lane * EPT + j;
-    }
-    below = wave::sum_i32(below);
-    if (below >= len) below = max(wave::max_i32(last_pos), 0);
-    if (lane == 0) {
-        exit_node[kd] = Vn;
-        bonus_token[kd] = c0 + below;
-    }
+__global__ __launch_bounds__(VOCAB_THREADS) void k_sample(SampleArgs<T> a) {
+    sample_wg<T, VEC>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // ----------------------------------------------------------------------------
@@ -668,51 +244,32 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_residual_cdf(
     }
 }
 
-ExitPtrs exit_ptrs(char *ws, int R, int B, int V) {
-    const ExitWs L = exit_ws_layout(R, B, V);
-    ExitPtrs p;
-    p.status = (unsigned *)(ws + L.status);
-    p.flags = (unsigned *)(ws + L.flags);
-    p.part_m = (float *)(ws + L.part_m);
-    p.row_m = (float *)(ws + L.row_m);
-    p.part_r = (double *)(ws + L.part_r);
-    p.part_c = (double *)(ws + L.part_c);
-    p.rcum = (double *)(ws + L.rcum);
-    p.wcum = (double *)(ws + L.wcum);
-    return p;
+template <typename T, bool VEC>
+void vocab_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R, int B,
+                int V, float sL, char *ws, hipStream_t st) {
+    const int nc = n_chunks(V);
+    k_vocab<T, VEC><<<dim3((nc + WAVES_PER_WG - 1) / WAVES_PER_WG, R * B), VOCAB_THREADS, 0, st>>>(
+        logits, parents, tokens, B, V, nc, sL, exit_ptrs(ws, R, B, V));
 }
 
-template <typename T, bool VEC>
-hipError_t exit_law_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R,
-                         int B, int V, float sL, float *rho, float *reach, float *w, float *cov,
-                         char *ws, hipStream_t st) {
-    const int nc = n_chunks(V);
-    const ExitPtrs P = exit_ptrs(ws, R, B, V);
-    k_vocab<T, VEC><<<dim3((nc + WAVES_PER_WG - 1) / WAVES_PER_WG, R * B), VOCAB_THREADS, 0, st>>>(
-        logits, parents, tokens, B, V, nc, sL, P);
-    const int nb = (B + REACH_WAVES * ROW_BATCH - 1) / (REACH_WAVES * ROW_BATCH);
-    if (nb <= 1)
-        k_reach<T, 1><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
-    else if (nb == 2)
-        k_reach<T, 2><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
-    else if (nb == 3)
-        k_reach<T, 3><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
-    else
-        k_reach<T, 4><<<dim3(R), REACH_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, P, rho, reach, w, cov);
-    return hipGetLastError();
+void reach_impl(const int32_t *parents, const int32_t *tokens, int R, int B, int V, float sL,
+                float *rho, float *reach, float *w, float *cov, char *ws, hipStream_t st) {
+    const ReachArgs a{parents, tokens, B, V, n_chunks(V), sL, exit_ptrs(ws, R, B, V), rho, reach, w, cov};
+    switch (reach_batches(B, REACH_THREADS)) {
+        case 1: k_reach<1><<<dim3(R), REACH_THREADS, 0, st>>>(a); break;
+        case 2: k_reach<2><<<dim3(R), REACH_THREADS, 0, st>>>(a); break;
+        case 3: k_reach<3><<<dim3(R), REACH_THREADS, 0, st>>>(a); break;
+        default: k_reach<4><<<dim3(R), REACH_THREADS, 0, st>>>(a); break;
+    }
 }
 
 template <typename T, bool VEC>
 hipError_t sample_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R,
                        int B, int V, float sL, const char *ws, const float *uniforms,
                        int n_draws, int32_t *exit_node, int32_t *bonus, hipStream_t st) {
-    const ExitWs L = exit_ws_layout(R, B, V);
-    const int nc = n_chunks(V);
-    k_sample<T, VEC><<<dim3((n_draws + WAVES_PER_WG - 1) / WAVES_PER_WG, R), VOCAB_THREADS, 0, st>>>(
-        logits, parents, tokens, B, V, nc, sL, (const unsigned *)(ws + L.status),
-        (const float *)(ws + L.part_m), (const double *)(ws + L.part_r),
-        (const float *)(ws + L.row_m), (const double *)(ws + L.rcum),
-        (const double *)(ws + L.wcum), uniforms, n_draws, exit_node, bonus);
+    const SampleArgs<T> a = sample_args(logits, parents, tokens, R, B, V, sL, ws, uniforms, n_draws,
+                                        exit_node, bonus);
+    k_sample<T, VEC><<<dim3((n_draws + WAVES_PER_WG - 1) / WAVES_PER_WG, R), VOCAB_THREADS, 0, st>>>(a);
     return hipGetLastError();
 }
 
@@ -731,18 +288,29 @@ hipError_t residual_cdf_impl(const T *logits, const int32_t *parents, const int3
 
 }  // namespace
 
+hipError_t launch_vocab(const void *logits, int dtype, bool vec, const int32_t *parents,
+                        const int32_t *tokens, int R, int B, int V, float sL, char *ws,
+                        hipStream_t st) {
+    if (dtype == TEV_BF16) {
+        const uint16_t *p = (const uint16_t *)logits;
+        if (vec) vocab_impl<uint16_t, true>(p, parents, tokens, R, B, V, sL, ws, st);
+        else vocab_impl<uint16_t, false>(p, parents, tokens, R, B, V, sL, ws, st);
+    } else {
+        const float *p = (const float *)logits;
+        if (vec) vocab_impl<float, true>(p, parents, tokens, R, B, V, sL, ws, st);
+        else vocab_impl<float, false>(p, parents, tokens, R, B, V, sL, ws, st);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_exit_law(const void *logits, int dtype, bool vec, const int32_t *parents,
                            const int32_t *tokens, int R, int B, int V, float sL, float *rho,
                            float *reach, float *exit_mass, float *coverage, char *ws,
                            hipStream_t st) {
-    if (dtype == TEV_BF16) {
-        const uint16_t *p = (const uint16_t *)logits;
-        return vec ? exit_law_impl<uint16_t, true>(p, parents, tokens, R, B, V, sL, rho, reach, exit_mass, coverage, ws, st)
-                   : exit_law_impl<uint16_t, false>(p, parents, tokens, R, B, V, sL, rho, reach, exit_mass, coverage, ws, st);
-    }
-    const float *p = (const float *)logits;
-    return vec ? exit_law_impl<float, true>(p, parents, tokens, R, B, V, sL, rho, reach, exit_mass, coverage, ws, st)
-               : exit_law_impl<float, false>(p, parents, tokens, R, B, V, sL, rho, reach, exit_mass, coverage, ws, st);
+    const hipError_t e = launch_vocab(logits, dtype, vec, parents, tokens, R, B, V, sL, ws, st);
+    if (e != hipSuccess) return e;
+    reach_impl(parents, tokens, R, B, V, sL, rho, reach, exit_mass, coverage, ws, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_sample(const void *logits, int dtype, bool vec, const int32_t *parents,

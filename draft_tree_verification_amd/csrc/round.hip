@@ -1,0 +1,156 @@
+// round.hip -- one whole verification round in three launches on gfx950.
+//
+// The round computes exactly what tev_tree_attn, tev_exit_law and tev_sample
+// compute one after the other (tree attention: "CAST: Cost-Aware Speculative
+// Trees from One-Pass Block Drafters", App. B Lemma 1 and App. C; exit law and
+// draws: "Where Draft Trees Lose Target Mass: Exit-Guided Speculative
+// Decoding", Sec. 3 Eq. 1-2, Sec. 3.1 Eq. 4, Sec. 3.2 Eq. 6-7, App. B
+// Algorithm 1), but packs the work so that the single-workgroup steps run
+// beside the wide ones instead of after them:
+//
+//   1. k_vocab                       -- the logit stream (all CUs);
+//   2. k_round_attn = attention workgroups + one reach workgroup per request:
+//      the attention plan leaves that many CUs free, and the reach needs only
+//      the vocabulary pass, finished by the stream order;
+//   3. k_round_tail = draw workgroups + the split combine of the attention:
+//      the draws need the reach, the combine the attention, both done.
+//
+// Workgroups of one launch never wait for each other, so no cross-workgroup
+// synchronisation is involved; the roles only share the launch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "exit_law_dev.h"
+#include "tev_internal.h"
+#include "tree_attn_dev.h"
+
+namespace tev {
+namespace {
+
+// Launch 2: workgroups [0, attn_grid) are attention tasks, the next R are the
+// reach of request b - attn_grid (512 threads, NB batches of rows).
+template <int D, int NQT, int NB>
+__global__ __launch_bounds__(NT) void k_round_attn(AttnArgs a, ReachArgs ra, int attn_grid) {
+    const int b = (int)blockIdx.x;
+    if (b >= attn_grid) {
+        reach_wg<NB, NT>(ra, b - attn_grid);
+        return;
+    }
+    const int task = xcd_task(b, a.n_wg);
+    if (task >= a.n_wg) return;
+    attn_mfma_wg<D, NQT>(a, task);
+}
+
+struct CombineArgs {
+    const float *part_o, *part_ml;
+    int splits, Hkv, G, B, Hq;
+    size_t rows_all;
+    const unsigned *status;
+    float *out;
+};
+
+// Launch 3: workgroups [0, R * sbx) draw (request b / sbx, draws 4 (b % sbx)
+// .. + 3), the rest combine the attention splits.
+template <int D, typename T, bool VEC>
+__global__ __launch_bounds__(VOCAB_THREADS) void k_round_tail(SampleArgs<T> sa, int sbx, int n_sample,
+                                                            CombineArgs ca) {
+    const int b = (int)blockIdx.x;
+    if (b < n_sample) {
+        sample_wg<T, VEC>(sa, b % sbx, b / sbx);
+        return;
+    }
+    attn_combine_wg<D>(ca.part_o, ca.part_ml, ca.splits, ca.Hkv, ca.G, ca.B, ca.Hq, ca.rows_all,
+                       ca.status, ca.out, b - n_sample);
+}
+
+template <int D, int NQT, int NB>
+void launch_round_attn(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R, hipStream_t st) {
+    k_round_attn<D, NQT, NB><<<dim3((unsigned)(attn_grid + R)), NT, 0, st>>>(a, ra, attn_grid);
+}
+
+template <int D, int NQT>
+void round_attn_nb(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R, int B, hipStream_t st) {
+    const int nb = reach_batches(B, NT);
+    if (nb <= 2) launch_round_attn<D, NQT, 2>(a, ra, attn_grid, R, st);
+    else if (nb <= 4) launch_round_attn<D, NQT, 4>(a, ra, attn_grid, R, st);
+    else launch_round_attn<D, NQT, 8>(a, ra, attn_grid, R, st);
+}
+
+template <int D, typename T, bool VEC>
+void launch_round_tail(const SampleArgs<T> &sa, int R, int n_draws, const CombineArgs &ca,
+                       int n_combine, hipStream_t st) {
+    const int sbx = (n_draws + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    const int n_sample = R * sbx;
+    k_round_tail<D, T, VEC><<<dim3((unsigned)(n_sample + n_combine)), VOCAB_THREADS, 0, st>>>(
+        sa, sbx, n_sample, ca);
+}
+
+template <int D, typename T>
+void round_tail_vec(bool vec, const SampleArgs<T> &sa, int R, int n_draws, const CombineArgs &ca,
+                    int n_combine, hipStream_t st) {
+    if (vec) launch_round_tail<D, T, true>(sa, R, n_draws, ca, n_combine, st);
+    else launch_round_tail<D, T, false>(sa, R, n_draws, ca, n_combine, st);
+}
+
+}  // namespace
+
+hipError_t launch_round(const void *q, const void *k, const void *v, const void *logits, int dtype,
+                        bool vec, const int32_t *parents, const int32_t *tokens, int R, int B,
+                        int V, int Hq, int Hkv, int D, int P, float scale, float sL,
+                        const float *uniforms, int n_draws, float *attn_out, float *rho,
+                        float *reach, float *exit_mass, float *coverage, int32_t *exit_node,
+                        int32_t *bonus_token, char *ws, hipStream_t st) {
+    const RoundWs RL = round_ws_layout(R, B, V, Hq, Hkv, D, P);
+    char *ws_e = ws + RL.exit;
+    char *ws_a = ws + RL.attn;
+    if (dtype != TEV_BF16) {
+        // fp32 attention runs on the vector ALU path: the three calls in order
+        hipError_t e = launch_exit_law(logits, dtype, vec, parents, tokens, R, B, V, sL, rho, reach,
+                                       exit_mass, coverage, ws_e, st);
+        if (e == hipSuccess)
+            e = launch_tree_attn(q, k, v, dtype, parents, R, B, Hq, Hkv, D, P, scale, attn_out, ws_a, st);
+        if (e == hipSuccess)
+            e = launch_sample(logits, dtype, vec, parents, tokens, R, B, V, sL, ws_e, uniforms,
+                              n_draws, exit_node, bonus_token, st);
+        return e;
+    }
+
+    // 1. the vocabulary pass
+    hipError_t e = launch_vocab(logits, dtype, vec, parents, tokens, R, B, V, sL, ws_e, st);
+    if (e != hipSuccess) return e;
+
+    // 2. attention + reach
+    const AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P, RL.reserve);
+    const AttnWs AL = attn_ws_layout(R, B, Hq, Hkv, D, P, RL.reserve);
+    float *part_o = (float *)(ws_a + AL.part_o);
+    float *part_ml = (float *)(ws_a + AL.part_ml);
+    unsigned *astatus = (unsigned *)(ws_a + AL.status);
+    const int n_wg = pl.row_blocks * pl.splits * R * Hkv;
+    const int attn_grid = 8 * ((n_wg + 7) / 8);
+    const float c_log2 = (float)((double)scale * 1.4426950408889634);
+    const AttnArgs a{(const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, parents, B, Hq, Hkv,
+                     P, c_log2, pl.row_blocks, pl.splits, pl.keys_per_split, n_wg, attn_out, part_o,
+                     part_ml, astatus};
+    const ReachArgs ra{parents, tokens, B, V, n_chunks(V), sL, exit_ptrs(ws_e, R, B, V), rho, reach,
+                       exit_mass, coverage};
+    if (D == 64 && pl.nqt == 1) round_attn_nb<64, 1>(a, ra, attn_grid, R, B, st);
+    else if (D == 64) round_attn_nb<64, 2>(a, ra, attn_grid, R, B, st);
+    else if (pl.nqt == 1) round_attn_nb<128, 1>(a, ra, attn_grid, R, B, st);
+    else round_attn_nb<128, 2>(a, ra, attn_grid, R, B, st);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    // 3. draws + split combine
+    const int G = Hq / Hkv;
+    const size_t rows_all = (size_t)R * Hkv * G * B;
+    const CombineArgs ca{part_o, part_ml, pl.splits, Hkv, G, B, Hq, rows_all, astatus, attn_out};
+    const int n_combine = pl.splits > 1 ? (int)((rows_all + 3) / 4) : 0;
+    const SampleArgs<uint16_t> sa = sample_args((const uint16_t *)logits, parents, tokens, R, B, V, sL,
+                                                ws_e, uniforms, n_draws, exit_node, bonus_token);
+    if (D == 64) round_tail_vec<64, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
+    else round_tail_vec<128, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
+    return hipGetLastError();
+}
+
+}  // namespace tev

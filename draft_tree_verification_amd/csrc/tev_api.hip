@@ -115,6 +115,41 @@ tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
                                        (char *)workspace, (hipStream_t)stream));
 }
 
+size_t tev_verify_round_workspace_bytes(int R, int B, int V, int Hq, int Hkv, int D, int P) {
+    if (check_exit_shape(R, B, V) != TEV_OK) return 0;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0 || (D != 64 && D != 128)) return 0;
+    return round_ws_layout(R, B, V, Hq, Hkv, D, P).total;
+}
+
+tev_status tev_verify_round(const void *q, const void *k, const void *v, const void *logits,
+                            int dtype, const int32_t *parents, const int32_t *tokens, int R, int B,
+                            int V, int Hq, int Hkv, int D, int P, float scale,
+                            float inv_temperature, const float *uniforms, int n_draws,
+                            float *attn_out, float *rho, float *reach, float *exit_mass,
+                            float *coverage, int32_t *exit_node, int32_t *bonus_token,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k || !v || !logits || !parents || !tokens || !uniforms || !attn_out || !rho ||
+        !reach || !exit_mass || !coverage || !exit_node || !bonus_token || !workspace)
+        return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    if (Hq < 1 || Hkv < 1 || P < 0 || Hq % Hkv) return TEV_ERR_SHAPE;
+    if ((long long)R * Hkv > 65535 || (long long)P + B > (1LL << 30)) return TEV_ERR_SHAPE;
+    if (n_draws < 1 || n_draws > 65535) return TEV_ERR_SHAPE;
+    if (D != 64 && D != 128) return TEV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return TEV_ERR_VALUE;
+    if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
+    if (dtype == TEV_BF16 &&
+        (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)attn_out) % 16))
+        return TEV_ERR_UNSUPPORTED;
+    if (workspace_bytes < round_ws_layout(R, B, V, Hq, Hkv, D, P).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_round(q, k, v, logits, dtype, vec_ok(logits, dtype, V), parents, tokens,
+                                   R, B, V, Hq, Hkv, D, P, scale, log2e_scale(inv_temperature),
+                                   uniforms, n_draws, attn_out, rho, reach, exit_mass, coverage,
+                                   exit_node, bonus_token, (char *)workspace, (hipStream_t)stream));
+}
+
 tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host, int B,
                                   int V) {
     if (!parents_host || !tokens_host) return TEV_ERR_NULL;
@@ -133,16 +168,25 @@ tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *to
 
 tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
                                   uint32_t *flags_host, void *stream) {
-    (void)B;
-    (void)V;
     if (!workspace || !flags_host) return TEV_ERR_NULL;
     if (R < 1) return TEV_ERR_SHAPE;
-    if (kind != 0 && kind != 1) return TEV_ERR_SHAPE;
+    if (kind != 0 && kind != 1 && kind != 2) return TEV_ERR_SHAPE;
     // Both layouts place the status words first.
     hipError_t e = hipMemcpyAsync(flags_host, workspace, sizeof(uint32_t) * (size_t)R,
                                   hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
-    return hip_status(e);
+    if (e != hipSuccess || kind != 2) return hip_status(e);
+    if (check_exit_shape(R, B, V) != TEV_OK) return TEV_ERR_SHAPE;
+    // the round's workspace: the attention part follows the exit-law part
+    const size_t off = align_up(exit_ws_layout(R, B, V).total, 256);
+    for (int r = 0; r < R; r++) {
+        uint32_t fa = 0;
+        e = hipMemcpy(&fa, (const char *)workspace + off + sizeof(uint32_t) * r, sizeof(uint32_t),
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return TEV_ERR_HIP;
+        flags_host[r] |= fa;
+    }
+    return TEV_OK;
 }
 
 tev_status tev_export_exit_cdf(const void *workspace, int R, int B, int V, double *cdf_host,

@@ -10,6 +10,8 @@
 
 namespace tev {
 
+constexpr float kInf = __builtin_inff();
+
 // The vocabulary pass splits every logit row into chunks of CHUNK tokens; one
 // wavefront (64 lanes) reduces one (row, chunk) pair on its own, each lane
 // holding EPT = 64 elements in registers.  A workgroup of VOCAB_THREADS
@@ -25,14 +27,16 @@ inline int n_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }
 // Exit-law workspace, per request r, node v, chunk c (nc chunks per row):
 //   status  u32 [R]          device flag bits of the request (TEV_FLAG_*)
 //   flags   u32 [R][B][nc]   per-(row, chunk) flags from the vocabulary pass
-//   part_m  f32 [R][B][nc]   chunk offset M_c in log2 units (max logit * sL)
+//   part_m  f32 [R][B][nc]   chunk offset M_c in log2 units (floor of max logit * sL)
 //   part_r  f64 [R][B][nc]   chunk residual sum  sum_{a in c, a not child} 2^(l_a sL - M_c)
 //   part_c  f64 [R][B][nc]   chunk child sum     sum_{a in c, a child}     2^(l_a sL - M_c)
 //   row_m   f32 [R][B]       row offset M_v = max_c M_c
 //   rcum    f64 [R][B][nc]   running residual sum over chunks, units 2^(-M_v)
 //   wcum    f64 [R][B]       running exit mass over nodes in index order
+//   cterm   f32 [R][B][2]    node u's own term 2^(l sL - M_c) in its parent's
+//                            row and that chunk's offset M_c (u > 0)
 struct ExitWs {
-    size_t status, flags, part_m, part_r, part_c, row_m, rcum, wcum, total;
+    size_t status, flags, part_m, part_r, part_c, row_m, rcum, wcum, cterm, total;
 };
 
 inline ExitWs exit_ws_layout(int R, int B, int V) {
@@ -47,6 +51,7 @@ inline ExitWs exit_ws_layout(int R, int B, int V) {
     L.row_m = o;  o = align_up(o + 4 * rb, 256);
     L.rcum = o;   o = align_up(o + 8 * rbc, 256);
     L.wcum = o;   o = align_up(o + 8 * rb, 256);
+    L.cterm = o;  o = align_up(o + 8 * rb, 256);
     L.total = o;
     return L;
 }
@@ -60,17 +65,19 @@ struct AttnPlan {
     int rows_per_wg;      // 4 * nqt * 16 (two key groups share the rows)
     int row_blocks;       // ceil(G*B / rows_per_wg)
     int splits;           // prefix splits
-    int keys_per_split;   // multiple of 64 (one stage)
+    int keys_per_split;   // multiple of 32 (one block)
 };
 
 struct AttnWs {
     size_t status, part_o, part_ml, total;
 };
 
-AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P);
+// reserve: CUs the attention leaves free for other workgroups of the same
+// launch (the fused round runs the reach beside it).
+AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 0);
 
-inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P) {
-    AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P);
+inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 0) {
+    AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P, reserve);
     const int G = Hq / Hkv;
     const size_t rows = (size_t)R * Hkv * G * B;
     AttnWs L{};
@@ -83,7 +90,28 @@ inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P) {
     return L;
 }
 
+// Verification-round workspace: the exit-law workspace, then the attention
+// workspace of the plan that leaves the reach its CUs.
+struct RoundWs {
+    size_t exit, attn, total;
+    int reserve;
+};
+
+inline int round_reserve(int R) { return R < 8 ? R : 8; }
+
+inline RoundWs round_ws_layout(int R, int B, int V, int Hq, int Hkv, int D, int P) {
+    RoundWs L{};
+    L.reserve = round_reserve(R);
+    L.exit = 0;
+    L.attn = align_up(exit_ws_layout(R, B, V).total, 256);
+    L.total = L.attn + attn_ws_layout(R, B, Hq, Hkv, D, P, L.reserve).total;
+    return L;
+}
+
 // ---- launchers (return hipGetLastError() of the launches) ----
+hipError_t launch_vocab(const void *logits, int dtype, bool vec, const int32_t *parents,
+                        const int32_t *tokens, int R, int B, int V, float sL, char *ws,
+                        hipStream_t st);
 hipError_t launch_exit_law(const void *logits, int dtype, bool vec, const int32_t *parents,
                            const int32_t *tokens, int R, int B, int V, float sL, float *rho,
                            float *reach, float *exit_mass, float *coverage, char *ws,
@@ -98,5 +126,12 @@ hipError_t launch_residual_cdf(const void *logits, int dtype, bool vec, const in
 hipError_t launch_tree_attn(const void *q, const void *k, const void *v, int dtype,
                             const int32_t *parents, int R, int B, int Hq, int Hkv, int D, int P,
                             float scale, float *out, char *ws, hipStream_t st);
+
+hipError_t launch_round(const void *q, const void *k, const void *v, const void *logits, int dtype,
+                        bool vec, const int32_t *parents, const int32_t *tokens, int R, int B,
+                        int V, int Hq, int Hkv, int D, int P, float scale, float sL,
+                        const float *uniforms, int n_draws, float *attn_out, float *rho,
+                        float *reach, float *exit_mass, float *coverage, int32_t *exit_node,
+                        int32_t *bonus_token, char *ws, hipStream_t st);
 
 }  // namespace tev

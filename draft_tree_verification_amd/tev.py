@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "TEV_OK", 1: "TEV_ERR_NULL", 2: "TEV_ERR_SHAPE", 3: "TEV_ERR_
 EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
-            "tev_export_residual_cdf"]
+            "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round"]
 
 
 class TevError(RuntimeError):
@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.tev_status_str.restype = ctypes.c_char_p
         L.tev_export_exit_cdf.argtypes = [vp, i, i, i, vp, vp]
         L.tev_export_residual_cdf.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, i, i, vp, vp]
+        L.tev_verify_round_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.tev_verify_round_workspace_bytes.restype = sz
+        L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for fn in ("tev_exit_law", "tev_sample", "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
@@ -190,6 +194,66 @@ def tev_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: to
                              int(P), float(scale), _p(out), _p(workspace), workspace.numel(),
                              _stream())
     _check("tev_tree_attn", st)
+    return out
+
+
+# ---------------------------------------------------------------- whole round
+@dataclass
+class RoundResult:
+    attn_out: torch.Tensor     # float32 [R][B][Hq][D]
+    rho: torch.Tensor          # float32 [R][B]
+    reach: torch.Tensor        # float32 [R][B]
+    exit_mass: torch.Tensor    # float32 [R][B]
+    coverage: torch.Tensor     # float32 [R]
+    exit_node: torch.Tensor    # int32 [R][n]
+    bonus_token: torch.Tensor  # int32 [R][n]
+    workspace: torch.Tensor    # uint8; its head is an exit-law workspace
+
+
+def tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P) -> int:
+    return int(lib().tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P))
+
+
+def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                     parents: torch.Tensor, tokens: torch.Tensor, uniforms: torch.Tensor, P: int,
+                     scale: float | None = None, inv_temperature: float = 1.0,
+                     workspace: torch.Tensor | None = None,
+                     out: RoundResult | None = None) -> RoundResult:
+    """Tree attention, exit law and draws of one round (the three calls'
+    arguments; q/k/v and logits share one dtype)."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    _need_cuda(q, k, v, logits, parents, tokens, uniforms)
+    R, B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    V = logits.shape[-1]
+    if k.shape != (R, Hkv, P + B, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must be [R][Hkv][P+B][D] with q's dtype")
+    if logits.shape != (R, B, V) or logits.dtype != q.dtype:
+        raise ValueError("logits must be [R][B][V] with q's dtype")
+    n = uniforms.shape[-2]
+    if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * 2:
+        raise ValueError("uniforms must be float32 [R][n][2]")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    dev = q.device
+    if out is None:
+        if workspace is None:
+            need = tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P)
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = RoundResult(torch.empty((R, B, Hq, D), **f32), torch.empty((R, B), **f32),
+                          torch.empty((R, B), **f32), torch.empty((R, B), **f32),
+                          torch.empty((R,), **f32),
+                          torch.empty((R, n), dtype=torch.int32, device=dev),
+                          torch.empty((R, n), dtype=torch.int32, device=dev), workspace)
+    st = lib().tev_verify_round(_p(q), _p(k), _p(v), _p(logits), _dtype_code(q), _p(parents),
+                                _p(tokens), R, B, V, Hq, Hkv, D, int(P), float(scale),
+                                float(inv_temperature), _p(uniforms), n, _p(out.attn_out),
+                                _p(out.rho), _p(out.reach), _p(out.exit_mass), _p(out.coverage),
+                                _p(out.exit_node), _p(out.bonus_token), _p(out.workspace),
+                                out.workspace.numel(), _stream())
+    _check("tev_verify_round", st)
     return out
 
 

@@ -143,6 +143,34 @@ tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
                          void *stream);
 
 /* ------------------------------------------------------------------------
+ * One whole verification round: tree attention, exit law and draws.
+ *
+ * Computes exactly what tev_tree_attn, tev_exit_law and tev_sample compute,
+ * in that order, with the arguments of those calls (one dtype for both q/k/v
+ * and logits), into the same outputs.  The work is packed into three
+ * launches (vocabulary pass; attention beside the reach; draws beside the
+ * split combine), so the single-workgroup steps of the exit law overlap the
+ * attention instead of following it.
+ *
+ * workspace must hold tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P)
+ * bytes, any initial contents; calls sharing a workspace must not overlap.
+ * Its first tev_exit_law_workspace_bytes(R, B, V) bytes are an exit-law
+ * workspace: tev_sample, tev_export_exit_cdf and tev_export_residual_cdf
+ * accept it after the round.  tev_read_device_status with kind 2 returns the
+ * request's exit-law and attention flags together.
+ * Errors: as the three calls (host checks before anything is enqueued).
+ * ------------------------------------------------------------------------ */
+size_t tev_verify_round_workspace_bytes(int R, int B, int V, int Hq, int Hkv, int D, int P);
+
+tev_status tev_verify_round(const void *q, const void *k, const void *v, const void *logits,
+                            int dtype, const int32_t *parents, const int32_t *tokens, int R,
+                            int B, int V, int Hq, int Hkv, int D, int P, float scale,
+                            float inv_temperature, const float *uniforms, int n_draws,
+                            float *attn_out, float *rho, float *reach, float *exit_mass,
+                            float *coverage, int32_t *exit_node, int32_t *bonus_token,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
 
@@ -151,11 +179,11 @@ tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
 tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host,
                                   int B, int V);
 
-/* Copies the R per-request flag words (TEV_FLAG_*) of an exit-law or
- * tree-attention workspace into flags_host [R].  `kind` is 0 for an exit-law
- * workspace (sizes R, B, V) and 1 for a tree-attention workspace (B, Hq, Hkv,
- * D, P ignored for the lookup but R must match).  Synchronous: waits for
- * `stream`. */
+/* Copies the R per-request flag words (TEV_FLAG_*) of an exit-law,
+ * tree-attention or round workspace into flags_host [R].  `kind` is 0 for an
+ * exit-law workspace (sizes R, B, V), 1 for a tree-attention workspace (only R
+ * is used) and 2 for a tev_verify_round workspace (sizes R, B, V; the two
+ * parts' flags are OR-ed).  Synchronous: waits for `stream`. */
 tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
                                   uint32_t *flags_host, void *stream);
 

@@ -1,0 +1,102 @@
+"""GPU parity of tev_verify_round (one call for the whole round) through the
+C ABI: its attention output, exit law and draws against the CPU oracle under
+the same acceptance rules as the separate calls, and its exit law and draws
+bit-equal to those of tev_exit_law + tev_sample on the same inputs (the round
+runs the same arithmetic, only packed into fewer launches)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_tree_verification_amd import tev
+from draft_tree_verification_amd import workloads as W
+from tests import gpu_parity as GP
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(wl, a):
+    if wl.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def _run_round(wl, n_uniform=None):
+    q, k, v = _dev(wl, wl.q), _dev(wl, wl.k), _dev(wl, wl.v)
+    lg, par, tok, uni = GP.device_inputs(wl)
+    res = tev.tev_verify_round(q, k, v, lg, par, tok, uni, wl.P, wl.scale, wl.inv_temperature)
+    torch.cuda.synchronize()
+    flags = tev.tev_read_device_status(res.workspace, 2, wl.R, wl.B, wl.V)
+    return res, flags, (lg, par, tok, uni)
+
+
+def _check_round(wl, rows=None):
+    res, flags, (lg, par, tok, uni) = _run_round(wl)
+    assert np.all(flags == 0), flags
+    # attention against the oracle
+    ref = oracle.tree_attn(wl.q, wl.k, wl.v, wl.dtype, wl.parents, wl.P, wl.scale, rows=rows)
+    got = res.attn_out.cpu().numpy().reshape(-1, wl.D)
+    got = got if rows is None else got[rows]
+    err = GP.attn_row_errors(got, ref)
+    assert err.max() <= GP.TOL_REL, f"attention row error {err.max():.3e}"
+    # exit law and draws: bit-equal to the separate calls ...
+    el = tev.tev_exit_law(lg, par, tok, wl.inv_temperature)
+    en, bt = tev.tev_sample(lg, par, tok, el.workspace, uni, wl.inv_temperature)
+    torch.cuda.synchronize()
+    for name, a, b in (("rho", res.rho, el.rho), ("reach", res.reach, el.reach),
+                       ("exit_mass", res.exit_mass, el.exit_mass), ("coverage", res.coverage, el.coverage),
+                       ("exit_node", res.exit_node, en), ("bonus_token", res.bonus_token, bt)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy(), err_msg=name)
+    # ... and within the bar of the oracle
+    ora = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature)
+    GP.assert_close_rel("exit_mass", res.exit_mass.cpu().numpy(), ora.exit_mass)
+    GP.assert_close_rel("coverage", res.coverage.cpu().numpy(), ora.coverage)
+    GP.assert_close_rel("reach", res.reach.cpu().numpy(), ora.reach)
+    dr = oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, ora.exit_mass, wl.uniforms,
+                       wl.inv_temperature)
+    ok = ~(dr.band_exit | dr.band_bonus)
+    assert np.array_equal(res.exit_node.cpu().numpy()[ok], dr.exit_node[ok])
+    assert np.array_equal(res.bonus_token.cpu().numpy()[ok], dr.bonus_token[ok])
+    return float(err.max())
+
+
+SMALL = [
+    dict(name="bf16_d128", R=2, B=37, V=20000, Hq=8, Hkv=2, D=128, P=300, tree="random"),
+    dict(name="bf16_d64_best_first", R=1, B=64, V=17000, Hq=6, Hkv=3, D=64, P=517, tree="best_first"),
+    dict(name="bf16_max_nodes", R=1, B=256, V=9000, Hq=4, Hkv=2, D=128, P=1024, tree="random"),
+    dict(name="bf16_root_only", R=2, B=1, V=5000, Hq=4, Hkv=2, D=128, P=200, tree="random"),
+    dict(name="f32_small", R=2, B=16, V=3000, Hq=4, Hkv=4, D=64, P=128, tree="random", dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c["name"] for c in SMALL])
+def test_round_small(case):
+    c = dict(case)
+    name = c.pop("name")
+    dtype = c.pop("dtype", "bf16")
+    GP.log(f"[round] {name} {c} {dtype}")
+    wl = W.make_custom(name, dtype=dtype, n_uniform=512, **c)
+    err = _check_round(wl)
+    GP.log(f"[round] {name} ok, attention row error {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "mixture"])
+def test_round_named(name):
+    GP.log(f"[round] workload {name}")
+    wl = W.make_config(name, n_uniform=256)
+    rng = np.random.default_rng(1)
+    rows = np.unique(rng.integers(0, wl.R * wl.B * wl.Hq, size=64))
+    err = _check_round(wl, rows=rows)
+    GP.log(f"[round] {name} ok, attention row error {err:.3e}")
+
+
+def test_round_invalid_tree_is_flagged():
+    wl = W.make_custom("round_bad", R=2, B=12, V=9000, dtype="bf16", tree="random", Hq=4, Hkv=2,
+                       D=128, P=64, n_uniform=16)
+    wl.parents[1, 5] = 7
+    res, flags, _ = _run_round(wl)
+    assert flags[1] & tev.TEV_FLAG_TREE and flags[0] == 0
+    assert np.all(np.isnan(res.exit_mass[1].cpu().numpy()))
+    assert np.all(res.exit_node[1].cpu().numpy() == -1)
+    assert np.all(np.isnan(res.attn_out[1].cpu().numpy()))
+    assert np.all(np.isfinite(res.attn_out[0].cpu().numpy()))
