@@ -9,12 +9,13 @@ tev_sample).  The default workload is the Qwen3-4B-shaped round:
 1 request, B = 64 tree nodes (root included), V = 151936 bf16 logits, 32/8
 heads of dim 128 over a 4096-token KV prefix.
 
-Timing: each step's three calls are captured in a HIP graph per input copy;
-the copies form a ring larger than the 256 MB Infinity Cache, so every step
-reads its inputs from HBM.  The timed region is bracketed by a device
-synchronisation and HIP events on the stream the graphs are launched on.
-Per-call durations come from HIP events around graph replays of each call
-alone.
+Timing: each step is captured in a HIP graph per input copy; the copies form
+a ring larger than the 256 MB Infinity Cache, so every step reads its inputs
+from HBM.  The timed region is bracketed by a device synchronisation and HIP
+events on the stream the graphs are launched on.  The duration of each of the
+round's three launches (for the roofline of the dominant one) comes from HIP
+events that tev_verify_round_timed records at its launch boundaries; the
+separate calls are timed by graph replays of each call alone (context).
 
 The CPU baseline is the fp64 oracle timed on this host's cores on whole
 rounds of the same workload (bounded to about 10 s of CPU work).
@@ -42,6 +43,34 @@ CSRC = os.path.join(ROOT, "draft_tree_verification_amd", "csrc")
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvent:
+    """A HIP event without the system-scope release fence (timing enabled)."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            HipEvent._hip = h
+        ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(ev), HipEvent.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.cuda_event = ev.value
+
+    @staticmethod
+    def elapsed_us(a: "HipEvent", b: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a.cuda_event),
+                                             ctypes.c_void_p(b.cuda_event)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1e3
 
 
 def kernel_source_hash() -> str:
@@ -228,7 +257,25 @@ def main():
     value = R * B / (ms_per_step * 1e-3)
     log(f"[bench] {ms_per_step * 1e3:.2f} us per round -> {value / 1e6:.3f} M nodes/s")
 
-    # per-call durations (graph replays of one call, same ring, same stream)
+    # Launch durations of the round: tev_verify_round_timed records four HIP
+    # events at its launch boundaries.  The events skip the system-scope fence
+    # of a default event (which would add a cache flush to every boundary), so
+    # each interval is the launch plus its dispatch gap.  Rounds are enqueued
+    # back to back (the host runs ahead of the GPU), then read.
+    n_phase = max(args.call_iters, 2 * ring)
+    ev = [[HipEvent() for _ in range(4)] for _ in range(n_phase + 6)]
+    with torch.cuda.stream(stream):
+        for i, row in enumerate(ev):
+            sl = slots[i % ring]
+            tev.tev_verify_round(sl["q"], sl["k"], sl["v"], sl["lg"], sl["par"], sl["tok"], sl["uni"],
+                                 wl.P, wl.scale, wl.inv_temperature, out=round_out, events=row)
+    torch.cuda.synchronize()
+    names = ("k_vocab", "k_round_attn", "k_round_tail")
+    phase_us = {nm: float(np.mean([HipEvent.elapsed_us(row[j], row[j + 1]) for row in ev[6:]]))
+                for j, nm in enumerate(names)}
+    log("[bench] round launches (us): " + ", ".join(f"{k} {v:.2f}" for k, v in phase_us.items()))
+
+    # per-call durations of the three separate calls (graph replays, same ring)
     per_call = {}
     for name, fn in (("tev_tree_attn", call_attn), ("tev_exit_law", call_exit), ("tev_sample", call_sample)):
         gs = capture(fn)
@@ -249,35 +296,41 @@ def main():
     log(f"[bench] per call (us): " + ", ".join(f"{k} {v:.2f}" for k, v in per_call.items()))
 
     work = algorithmic_work(wl)
-    attn_us, exit_us = per_call["tev_tree_attn"], per_call["tev_exit_law"]
-    attn_gbs = work["attn_bytes"] / (attn_us * 1e-6) / 1e9
-    attn_tfs = work["attn_flops"] / (attn_us * 1e-6) / 1e12
-    exit_gbs = work["exit_law_bytes"] / (exit_us * 1e-6) / 1e9
     attn_hbm_bound = work["attn_bytes"] / HBM_PEAK_GBS > work["attn_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e3
+
+    def attn_roof(us):
+        gbs = work["attn_bytes"] / (us * 1e-6) / 1e9
+        tfs = work["attn_flops"] / (us * 1e-6) / 1e12
+        if attn_hbm_bound:
+            return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        return {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    def vocab_roof(us):
+        gbs = work["exit_law_bytes"] / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
     kernels = {
-        "tev_tree_attn": {"us": round(attn_us, 3), "bytes": work["attn_bytes"], "flops": work["attn_flops"],
-                          "GB/s": round(attn_gbs, 1), "TFLOP/s": round(attn_tfs, 2),
-                          "bound": "hbm" if attn_hbm_bound else "mfma",
-                          "frac": round(attn_gbs / HBM_PEAK_GBS if attn_hbm_bound else attn_tfs / MFMA_BF16_PEAK_TFLOPS, 4)},
-        "tev_exit_law": {"us": round(exit_us, 3), "bytes": work["exit_law_bytes"], "GB/s": round(exit_gbs, 1),
-                         "bound": "hbm", "frac": round(exit_gbs / HBM_PEAK_GBS, 4)},
-        "tev_sample": {"us": round(per_call["tev_sample"], 3)},
+        "k_vocab": dict(us=round(phase_us["k_vocab"], 3), bytes=work["exit_law_bytes"],
+                        **vocab_roof(phase_us["k_vocab"])),
+        "k_round_attn": dict(us=round(phase_us["k_round_attn"], 3), bytes=work["attn_bytes"],
+                             flops=work["attn_flops"], **attn_roof(phase_us["k_round_attn"]),
+                             note="attention workgroups + the reach workgroup of each request"),
+        "k_round_tail": {"us": round(phase_us["k_round_tail"], 3),
+                         "note": "draw workgroups + the attention split combine"},
+        "separate_calls_us": {k: round(v, 3) for k, v in per_call.items()},
     }
-    dominant = "tev_tree_attn" if attn_us >= exit_us else "tev_exit_law"
+    dominant = max(("k_vocab", "k_round_attn"), key=phase_us.get)
+    roof = dict(kernels[dominant])
+    for k_ in ("us", "bytes", "flops", "note"):
+        roof.pop(k_, None)
+    roof["kernel"] = dominant
+    roof["launch_us"] = round(phase_us[dominant], 3)
     src_hash = kernel_source_hash()
     traffic = load_traffic(wl.name, src_hash)
-    if dominant == "tev_tree_attn":
-        if attn_hbm_bound:
-            roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
-        else:
-            roof = {"bound": "mfma", "achieved": round(attn_tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(attn_tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(exit_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(exit_gbs / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = dominant
-    roof["traffic"] = (traffic or {}).get(dominant, {}).get("bytes_per_launch") if traffic else None
+    roof["traffic"] = traffic.get(dominant, {}).get("bytes_per_launch") if traffic else None
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -100,8 +100,12 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
                         int V, int Hq, int Hkv, int D, int P, float scale, float sL,
                         const float *uniforms, int n_draws, float *attn_out, float *rho,
                         float *reach, float *exit_mass, float *coverage, int32_t *exit_node,
-                        int32_t *bonus_token, char *ws, hipStream_t st) {
+                        int32_t *bonus_token, char *ws, hipStream_t st, void *const *events) {
     const RoundWs RL = round_ws_layout(R, B, V, Hq, Hkv, D, P);
+    // optional caller events at the launch boundaries (profiling)
+    auto mark = [&](int i) {
+        if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], st);
+    };
     char *ws_e = ws + RL.exit;
     char *ws_a = ws + RL.attn;
     if (dtype != TEV_BF16) {
@@ -117,8 +121,10 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
     }
 
     // 1. the vocabulary pass
+    mark(0);
     hipError_t e = launch_vocab(logits, dtype, vec, parents, tokens, R, B, V, sL, ws_e, st);
     if (e != hipSuccess) return e;
+    mark(1);
 
     // 2. attention + reach
     const AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P, RL.reserve);
@@ -140,6 +146,7 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
     else round_attn_nb<128, 2>(a, ra, attn_grid, R, B, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    mark(2);
 
     // 3. draws + split combine
     const int G = Hq / Hkv;
@@ -150,7 +157,9 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
                                                 ws_e, uniforms, n_draws, exit_node, bonus_token);
     if (D == 64) round_tail_vec<64, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
     else round_tail_vec<128, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
-    return hipGetLastError();
+    e = hipGetLastError();
+    mark(3);
+    return e;
 }
 
 }  // namespace tev

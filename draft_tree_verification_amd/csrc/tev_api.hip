@@ -121,13 +121,14 @@ size_t tev_verify_round_workspace_bytes(int R, int B, int V, int Hq, int Hkv, in
     return round_ws_layout(R, B, V, Hq, Hkv, D, P).total;
 }
 
-tev_status tev_verify_round(const void *q, const void *k, const void *v, const void *logits,
+tev_status tev_verify_round_timed(const void *q, const void *k, const void *v, const void *logits,
                             int dtype, const int32_t *parents, const int32_t *tokens, int R, int B,
                             int V, int Hq, int Hkv, int D, int P, float scale,
                             float inv_temperature, const float *uniforms, int n_draws,
                             float *attn_out, float *rho, float *reach, float *exit_mass,
                             float *coverage, int32_t *exit_node, int32_t *bonus_token,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                                  void *workspace, size_t workspace_bytes, void *stream,
+                                  void *const *events) {
     if (!q || !k || !v || !logits || !parents || !tokens || !uniforms || !attn_out || !rho ||
         !reach || !exit_mass || !coverage || !exit_node || !bonus_token || !workspace)
         return TEV_ERR_NULL;
@@ -147,7 +148,21 @@ tev_status tev_verify_round(const void *q, const void *k, const void *v, const v
     return hip_status(launch_round(q, k, v, logits, dtype, vec_ok(logits, dtype, V), parents, tokens,
                                    R, B, V, Hq, Hkv, D, P, scale, log2e_scale(inv_temperature),
                                    uniforms, n_draws, attn_out, rho, reach, exit_mass, coverage,
-                                   exit_node, bonus_token, (char *)workspace, (hipStream_t)stream));
+                                   exit_node, bonus_token, (char *)workspace, (hipStream_t)stream,
+                                   events));
+}
+
+tev_status tev_verify_round(const void *q, const void *k, const void *v, const void *logits,
+                            int dtype, const int32_t *parents, const int32_t *tokens, int R, int B,
+                            int V, int Hq, int Hkv, int D, int P, float scale,
+                            float inv_temperature, const float *uniforms, int n_draws,
+                            float *attn_out, float *rho, float *reach, float *exit_mass,
+                            float *coverage, int32_t *exit_node, int32_t *bonus_token,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    return tev_verify_round_timed(q, k, v, logits, dtype, parents, tokens, R, B, V, Hq, Hkv, D, P,
+                                  scale, inv_temperature, uniforms, n_draws, attn_out, rho, reach,
+                                  exit_mass, coverage, exit_node, bonus_token, workspace,
+                                  workspace_bytes, stream, nullptr);
 }
 
 tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host, int B,

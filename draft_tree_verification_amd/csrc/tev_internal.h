@@ -73,10 +73,12 @@ struct AttnWs {
 };
 
 // reserve: CUs the attention leaves free for other workgroups of the same
-// launch (the fused round runs the reach beside it).
-AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 0);
+// launch (the fused round runs the reach beside it).  The stand-alone call
+// keeps one free as well: with whole-block splits the last split, which also
+// holds the masked tree keys, then gets the short remainder of the prefix.
+AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 1);
 
-inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 0) {
+inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P, int reserve = 1) {
     AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P, reserve);
     const int G = Hq / Hkv;
     const size_t rows = (size_t)R * Hkv * G * B;
@@ -97,7 +99,7 @@ struct RoundWs {
     int reserve;
 };
 
-inline int round_reserve(int R) { return R < 8 ? R : 8; }
+inline int round_reserve(int R) { return R < 8 ? (R > 1 ? R : 1) : 8; }
 
 inline RoundWs round_ws_layout(int R, int B, int V, int Hq, int Hkv, int D, int P) {
     RoundWs L{};
@@ -132,6 +134,7 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
                         int V, int Hq, int Hkv, int D, int P, float scale, float sL,
                         const float *uniforms, int n_draws, float *attn_out, float *rho,
                         float *reach, float *exit_mass, float *coverage, int32_t *exit_node,
-                        int32_t *bonus_token, char *ws, hipStream_t st);
+                        int32_t *bonus_token, char *ws, hipStream_t st,
+                        void *const *events = nullptr);
 
 }  // namespace tev

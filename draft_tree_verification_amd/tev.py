@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "TEV_OK", 1: "TEV_ERR_NULL", 2: "TEV_ERR_SHAPE", 3: "TEV_ERR_
 EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
-            "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round"]
+            "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
+            "tev_verify_round_timed"]
 
 
 class TevError(RuntimeError):
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round_workspace_bytes.restype = sz
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
         for fn in ("tev_exit_law", "tev_sample", "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
@@ -218,9 +220,11 @@ def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: 
                      parents: torch.Tensor, tokens: torch.Tensor, uniforms: torch.Tensor, P: int,
                      scale: float | None = None, inv_temperature: float = 1.0,
                      workspace: torch.Tensor | None = None,
-                     out: RoundResult | None = None) -> RoundResult:
+                     out: RoundResult | None = None, events=None) -> RoundResult:
     """Tree attention, exit law and draws of one round (the three calls'
-    arguments; q/k/v and logits share one dtype)."""
+    arguments; q/k/v and logits share one dtype).  events: optional four
+    recorded-once torch.cuda.Event objects, re-recorded at the launch
+    boundaries (tev_verify_round_timed)."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
     _need_cuda(q, k, v, logits, parents, tokens, uniforms)
@@ -247,13 +251,17 @@ def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: 
                           torch.empty((R,), **f32),
                           torch.empty((R, n), dtype=torch.int32, device=dev),
                           torch.empty((R, n), dtype=torch.int32, device=dev), workspace)
-    st = lib().tev_verify_round(_p(q), _p(k), _p(v), _p(logits), _dtype_code(q), _p(parents),
-                                _p(tokens), R, B, V, Hq, Hkv, D, int(P), float(scale),
-                                float(inv_temperature), _p(uniforms), n, _p(out.attn_out),
-                                _p(out.rho), _p(out.reach), _p(out.exit_mass), _p(out.coverage),
-                                _p(out.exit_node), _p(out.bonus_token), _p(out.workspace),
-                                out.workspace.numel(), _stream())
-    _check("tev_verify_round", st)
+    args = [_p(q), _p(k), _p(v), _p(logits), _dtype_code(q), _p(parents), _p(tokens), R, B, V, Hq,
+            Hkv, D, int(P), float(scale), float(inv_temperature), _p(uniforms), n, _p(out.attn_out),
+            _p(out.rho), _p(out.reach), _p(out.exit_mass), _p(out.coverage), _p(out.exit_node),
+            _p(out.bonus_token), _p(out.workspace), out.workspace.numel(), _stream()]
+    if events is None:
+        st = lib().tev_verify_round(*args)
+        _check("tev_verify_round", st)
+    else:
+        handles = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib().tev_verify_round_timed(*args, ctypes.cast(handles, ctypes.c_void_p))
+        _check("tev_verify_round_timed", st)
     return out
 
 

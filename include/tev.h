@@ -170,6 +170,19 @@ tev_status tev_verify_round(const void *q, const void *k, const void *v, const v
                             float *coverage, int32_t *exit_node, int32_t *bonus_token,
                             void *workspace, size_t workspace_bytes, void *stream);
 
+/* tev_verify_round, and for profiling: events[0..3] (hipEvent_t, created by
+ * the caller, any entry may be NULL) are recorded on `stream` before the
+ * vocabulary pass, after it, after the attention launch and after the last
+ * launch, so that the caller can time each launch.  events may be NULL. */
+tev_status tev_verify_round_timed(const void *q, const void *k, const void *v,
+                                  const void *logits, int dtype, const int32_t *parents,
+                                  const int32_t *tokens, int R, int B, int V, int Hq, int Hkv,
+                                  int D, int P, float scale, float inv_temperature,
+                                  const float *uniforms, int n_draws, float *attn_out,
+                                  float *rho, float *reach, float *exit_mass, float *coverage,
+                                  int32_t *exit_node, int32_t *bonus_token, void *workspace,
+                                  size_t workspace_bytes, void *stream, void *const *events);
+
 /* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
