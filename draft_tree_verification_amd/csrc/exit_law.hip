@@ -70,24 +70,19 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
     const int32_t *par = parents + (size_t)r * B;
     const int32_t *tok = tokens + (size_t)r * B;
 
+    // The tree arrays first (a few hundred bytes, cache-resident after the
+    // first waves): the child mask below is then built while the logits are
+    // still in flight.  Unconditional loads of clamped indices.
+    int cpar[NPL], ctok[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        const int uc = min(1 + lane + 64 * k, B - 1);
+        cpar[k] = par[uc];
+        ctok[k] = tok[uc];
+    }
     const T *row = logits + (size_t)rv * (size_t)V + c0;
     float x[EPT];
-#pragma unroll
-    for (int k = 0; k < NV; k++) {
-        const int idx = k * SPAN + lane * VW;
-        if (VEC) {
-            if (idx < len) {
-                load16(row + idx, &x[k * VW]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < VW; j++) x[k * VW + j] = -kInf;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < VW; j++)
-                x[k * VW + j] = (idx + j < len) ? to_f32<T>(row[idx + j]) : -kInf;
-        }
-    }
+    load_chunk<T, VEC>(row, len, lane, x);
     s_mask[wave][2 * lane] = 0u;
     s_mask[wave][2 * lane + 1] = 0u;
     wave::lds_sync();
@@ -95,18 +90,18 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
     int mine_o[NPL];   // chunk offset of child 1 + lane + 64 k, or -1
 #pragma unroll
     for (int k = 0; k < NPL; k++) {
-        mine_o[k] = -1;
-        const int u = 1 + lane + 64 * k;
-        if (u < B && par[u] == v) {
-            const int o = tok[u] - c0;
-            if (o >= 0 && o < len) {
-                mine_o[k] = o;
-                const int kk = o / SPAN, rem = o - kk * SPAN;
-                const int bitpos = kk * VW + (rem % VW);           // 0..63 within the owner lane
-                const unsigned bit = 1u << (bitpos & 31);
-                const unsigned old = atomicOr(&s_mask[wave][2 * (rem / VW) + (bitpos >> 5)], bit);
-                dup |= (old & bit) != 0u;
-            }
+        // the test is evaluated outside the branch, so that the tree loads
+        // cannot sink into it (a load inside the branch would wait for the
+        // logits too)
+        const int o = ctok[k] - c0;
+        const bool hit = (1 + lane + 64 * k < B) & (cpar[k] == v) & (o >= 0) & (o < len);
+        mine_o[k] = hit ? o : -1;
+        if (hit) {
+            const int kk = o / SPAN, rem = o - kk * SPAN;
+            const int bitpos = kk * VW + (rem % VW);           // 0..63 within the owner lane
+            const unsigned bit = 1u << (bitpos & 31);
+            const unsigned old = atomicOr(&s_mask[wave][2 * (rem / VW) + (bitpos >> 5)], bit);
+            dup |= (old & bit) != 0u;
         }
     }
     wave::lds_sync();

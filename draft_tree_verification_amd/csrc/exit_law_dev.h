@@ -352,6 +352,34 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
 // is computed exactly as in the chunk pass (same f32 operations and offset);
 // child tokens are zero (bit j of the lane's mask word).
 // ----------------------------------------------------------------------------
+// The in-chunk element (i, j) of lane `lane` for the vocabulary pass's
+// interleaved ownership: elements k*(64*VW) + lane*VW + j, k < EPT/VW.  Every
+// load is unconditional: out-of-range elements read a clamped, valid address
+// and become -inf afterwards (a conditional load would make the compiler wait
+// for each load before issuing the next).
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_chunk(const T *chunk, int len, int lane, float *x) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    constexpr int SPAN = 64 * VW;
+#pragma unroll
+    for (int k = 0; k < EPT / VW; k++) {
+        const int idx = k * SPAN + lane * VW;
+        if (VEC) {
+            // len is a multiple of VW here (16-byte rows), so len - VW is a valid vector
+            load16(chunk + min(idx, len - VW), &x[k * VW]);
+#pragma unroll
+            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
+        } else {
+#pragma unroll
+            for (int j = 0; j < VW; j++) {
+                const float t = to_f32<T>(chunk[min(idx + j, len - 1)]);
+                x[k * VW + j] = (idx + j < len) ? t : -kInf;
+            }
+        }
+    }
+}
+
+// The sampler's contiguous ownership: lane t holds elements [64t, 64t + 64).
 template <typename T, bool VEC>
 __device__ __forceinline__ void segment_load(const T *chunk, int len, int lane, float *x) {
     constexpr int VW = 16 / (int)sizeof(T);
@@ -360,18 +388,19 @@ __device__ __forceinline__ void segment_load(const T *chunk, int len, int lane, 
     for (int k = 0; k < EPT / VW; k++) {
         const int idx = base + k * VW;
         if (VEC) {
-            if (idx < len) {
-                load16(chunk + idx, &x[k * VW]);
-            } else {
+            load16(chunk + min(idx, len - VW), &x[k * VW]);
 #pragma unroll
-                for (int j = 0; j < VW; j++) x[k * VW + j] = -kInf;
-            }
+            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
         } else {
 #pragma unroll
-            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx + j < len) ? to_f32<T>(chunk[idx + j]) : -kInf;
+            for (int j = 0; j < VW; j++) {
+                const float t = to_f32<T>(chunk[min(idx + j, len - 1)]);
+                x[k * VW + j] = (idx + j < len) ? t : -kInf;
+            }
         }
     }
 }
+
 __device__ __forceinline__ void segment_terms(const float *x, float sL, float Mc, uint64_t bits,
                                               float *e) {
     const float off = (Mc > -kInf) ? Mc : 0.f;   // a chunk of -inf logits has only zero terms
