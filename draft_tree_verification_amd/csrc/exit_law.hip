@@ -23,10 +23,10 @@
 //   fp64 (their logits gathered while the row pass runs), the reach P by
 //   pointer jumping along root paths, w, C and the exit CDF.
 //
-// k_sample -- one wave per (draw, request), loads in three dependent rounds:
-// exit draw over the node CDF, chunk search over the row's running residual
-// sums, then an fp64 wave scan inside the one chunk that holds the bonus
-// token.
+// k_sample -- one 256-thread workgroup per (draw, request), loads in three
+// dependent rounds: exit draw over the node CDF, chunk search over the row's
+// running residual sums, then an fp64 scan by the four waves together inside
+// the one chunk that holds the bonus token.
 //
 // Numerics: sL = fl(s * log2 e); each element contributes
 // 2^(fma(l, sL, -M_c)) with one rounding of the shifted exponent, M_c being
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(REACH_THREADS) void k_reach(ReachArgs a) {
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(VOCAB_THREADS) void k_sample(SampleArgs<T> a) {
+__global__ __launch_bounds__(SAMPLE_THREADS) void k_sample(SampleArgs<T> a) {
     sample_wg<T, VEC>(a, (int)blockIdx.x, (int)blockIdx.y);
 }
 
@@ -264,7 +264,7 @@ hipError_t sample_impl(const T *logits, const int32_t *parents, const int32_t *t
                        int n_draws, int32_t *exit_node, int32_t *bonus, hipStream_t st) {
     const SampleArgs<T> a = sample_args(logits, parents, tokens, R, B, V, sL, ws, uniforms, n_draws,
                                         exit_node, bonus);
-    k_sample<T, VEC><<<dim3((n_draws + WAVES_PER_WG - 1) / WAVES_PER_WG, R), VOCAB_THREADS, 0, st>>>(a);
+    k_sample<T, VEC><<<dim3(n_draws, R), SAMPLE_THREADS, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -24,10 +24,10 @@
 //   fp64 (their logits gathered while the row pass runs), the reach P by
 //   pointer jumping along root paths, w, C and the exit CDF.
 //
-// k_sample -- one wave per (draw, request), loads in three dependent rounds:
-// exit draw over the node CDF, chunk search over the row's running residual
-// sums, then an fp64 wave scan inside the one chunk that holds the bonus
-// token.
+// k_sample -- one 256-thread workgroup per (draw, request), loads in three
+// dependent rounds: exit draw over the node CDF, chunk search over the row's
+// running residual sums, then an fp64 scan by the four waves together inside
+// the one chunk that holds the bonus token.
 //
 // Numerics: sL = fl(s * log2 e); each element contributes
 // 2^(fma(l, sL, -M_c)) with one rounding of the shifted exponent, M_c being
@@ -468,57 +468,59 @@ struct SampleArgs {
     int32_t *exit_node, *bonus_token;
 };
 
-// Workgroup bx of request r (256 threads): wave w takes draw 4 bx + w.
+// Sum of one int per thread over a 256-thread workgroup (every thread gets
+// it); red is a 4-entry LDS scratch, reused only after a barrier.
+__device__ __forceinline__ int block_sum_i32(int x, int *red) {
+    const int w = wave::sum_i32(x);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    __syncthreads();
+    const int t = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    return t;
+}
+
+// Draw n of request r by one 256-thread workgroup (4 waves).  Loads come in
+// three dependent rounds, each issued as one group of unconditional loads:
+// (1) everything that does not depend on the draw, (2) the exit node's running
+// residual sums, (3) the one chunk that holds the bonus token, which the four
+// waves scan together (thread t owns tokens [16 t, 16 t + 16) of it).
+constexpr int SAMPLE_THREADS = 256;
+constexpr int SPT = CHUNK / SAMPLE_THREADS;   // 16 tokens per thread
+
 template <typename T, bool VEC>
-__device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int bx, const int r) {
+__device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, const int r) {
     const T *__restrict__ logits = A.logits;
     const int32_t *__restrict__ parents = A.parents;
     const int32_t *__restrict__ tokens = A.tokens;
     const int B = A.B, V = A.V, nc = A.nc;
     const float sL = A.sL;
-    const unsigned *__restrict__ status = A.status;
-    const float *__restrict__ part_m = A.part_m;
     const double *__restrict__ part_r = A.part_r;
-    const float *__restrict__ row_m = A.row_m;
     const double *__restrict__ rcum = A.rcum;
     const double *__restrict__ wcum = A.wcum;
-    const float *__restrict__ uniforms = A.uniforms;
     const int n_draws = A.n_draws;
-    int32_t *__restrict__ exit_node = A.exit_node;
-    int32_t *__restrict__ bonus_token = A.bonus_token;
-    const int wave_id = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n = bx * WAVES_PER_WG + wave_id;
-    __shared__ unsigned s_mask[WAVES_PER_WG][128];
-    if (n >= n_draws) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int s_red[4];
+    __shared__ double s_wsum[4];
+    __shared__ unsigned s_bits[SAMPLE_THREADS];
     const size_t kd = (size_t)r * n_draws + n;
-    // Loads in three rounds, each issued as one group: (1) everything that
-    // does not depend on the draw, (2) the exit node's running residual sums,
-    // (3) the one chunk that holds the bonus token.
-    const unsigned st = status[r];
-    const double u1 = (double)uniforms[2 * kd];
-    const double u2 = (double)uniforms[2 * kd + 1];
+
+    // ---- round 1 ----
+    const unsigned st = A.status[r];
+    const double u1 = (double)A.uniforms[2 * kd];
+    const double u2 = (double)A.uniforms[2 * kd + 1];
     const double *Wc = wcum + (size_t)r * B;
     const double Wtot = Wc[B - 1];
-    double wv[NPL];
-    int cpar[NPL], ctok[NPL];
-#pragma unroll
-    for (int k = 0; k < NPL; k++) {
-        const int j = lane + 64 * k, u = 1 + j;
-        wv[k] = (j < B) ? Wc[j] : 0.0;
-        cpar[k] = (u < B) ? parents[(size_t)r * B + u] : -1;
-        ctok[k] = (u < B) ? tokens[(size_t)r * B + u] : 0;
-    }
+    const double wj = Wc[min(tid, B - 1)];                      // node tid (B <= 256)
+    const int ui = min(1 + tid, B - 1);
+    const int cpar = parents[(size_t)r * B + ui];               // node 1 + tid
+    const int ctok = tokens[(size_t)r * B + ui];
     if (st != 0u) {
-        if (lane == 0) { exit_node[kd] = -1; bonus_token[kd] = -1; }
+        if (tid == 0) { A.exit_node[kd] = -1; A.bonus_token[kd] = -1; }
         return;
     }
-
     // Exit node: the number of j with W_j <= u1 * S is the smallest j with u1 S < W_j.
     const double t1 = u1 * Wtot;
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < NPL; k++) cnt += (lane + 64 * k < B && wv[k] <= t1) ? 1 : 0;
-    int Vn = wave::sum_i32(cnt);
+    int Vn = block_sum_i32((tid < B && wj <= t1) ? 1 : 0, s_red);
     if (Vn >= B) {   // rounding left no bin: last node with positive mass
         int best = -1;
         for (int j = lane; j < B; j += 64)
@@ -526,48 +528,96 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int bx, 
         Vn = max(wave::max_i32(best), 0);
     }
 
-    // Bonus token: the chunk whose running residual sum first exceeds u2 * T.
+    // ---- round 2: the chunk whose running residual sum first exceeds u2 * T ----
     const size_t rb = (size_t)r * B + Vn;
     const double *RC = rcum + rb * nc;
     const double t2 = u2 * RC[nc - 1];
-    int cc = 0;
-    for (int c = lane; c < nc; c += 64) cc += (RC[c] <= t2) ? 1 : 0;
-    cc = wave::sum_i32(cc);
+    int ccount = 0;
+    for (int c0 = 0; c0 < nc; c0 += SAMPLE_THREADS) {
+        const int c = c0 + tid;
+        const double rc = RC[min(c, nc - 1)];
+        ccount += (c < nc && rc <= t2) ? 1 : 0;
+    }
+    int cc = block_sum_i32(ccount, s_red);
     if (cc >= nc) {
         int best = -1;
         for (int c = lane; c < nc; c += 64)
             if (part_r[rb * nc + c] > 0.0) best = max(best, c);
         cc = max(wave::max_i32(best), 0);
     }
+
+    // ---- round 3: the chunk ----
     const int c0 = cc * CHUNK;
     const int len = min(CHUNK, V - c0);
-    float x[EPT];
-    segment_load<T, VEC>(logits + rb * (size_t)V + c0, len, lane, x);
-    const double before = (cc > 0) ? RC[cc - 1] : 0.0;
-    const float Mv = row_m[rb];
-    const float Mc = part_m[rb * nc + cc];
+    const T *chunk = logits + rb * (size_t)V + c0;
+    float x[SPT];
+    {
+        constexpr int VW = 16 / (int)sizeof(T);
+#pragma unroll
+        for (int k = 0; k < SPT / VW; k++) {
+            const int idx = tid * SPT + k * VW;
+            if (VEC) {
+                load16(chunk + min(idx, len - VW), &x[k * VW]);
+#pragma unroll
+                for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
+            } else {
+#pragma unroll
+                for (int j = 0; j < VW; j++) {
+                    const float t = to_f32<T>(chunk[min(idx + j, len - 1)]);
+                    x[k * VW + j] = (idx + j < len) ? t : -kInf;
+                }
+            }
+        }
+    }
+    const double rc_prev = RC[max(cc - 1, 0)];   // unconditional, issued with the chunk
+    const float Mv = A.row_m[rb];
+    const float Mc = A.part_m[rb * nc + cc];
+    const double before = (cc > 0) ? rc_prev : 0.0;
     // offsets are integers with Mc <= Mv: the rescale is an exact power of two
     const double target = __builtin_ldexp(t2 - before, (int)fminf(Mv - Mc, 2000.f));
 
-    const uint64_t bits = child_bits_regs(cpar, ctok, Vn, c0, len, s_mask[wave_id], lane);
-    float e[EPT];
-    segment_terms(x, sL, Mc, bits, e);
+    // child tokens of Vn inside the chunk: bit j of word t marks token 16 t + j
+    s_bits[tid] = 0u;
+    __syncthreads();
+    {
+        const int o = ctok - c0;
+        if ((1 + tid < B) & (cpar == Vn) & (o >= 0) & (o < len)) atomicOr(&s_bits[o / SPT], 1u << (o % SPT));
+    }
+    __syncthreads();
+    const unsigned bits = s_bits[tid];
+    const float off = (Mc > -kInf) ? Mc : 0.f;   // a chunk of -inf logits has only zero terms
+    float e[SPT];
     double seg = 0.0;
 #pragma unroll
-    for (int j = 0; j < EPT; j++) seg += (double)e[j];
-    double run = wave::incl_scan_f64(seg, lane) - seg;
+    for (int j = 0; j < SPT; j++) {
+        const float t = __builtin_amdgcn_exp2f(fmaf(x[j], sL, -off));
+        e[j] = ((bits >> j) & 1u) ? 0.f : t;
+        seg += (double)e[j];
+    }
+    // running sum in token order: in-wave scan, then the totals of earlier waves
+    const double incl = wave::incl_scan_f64(seg, lane);
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    double carry = 0.0;
+    for (int w = 0; w < wave; w++) carry += s_wsum[w];
+    double run = carry + incl - seg;
     int below = 0, last_pos = -1;
 #pragma unroll
-    for (int j = 0; j < EPT; j++) {
+    for (int j = 0; j < SPT; j++) {
         run += (double)e[j];
         below += (run <= target) ? 1 : 0;
-        if (e[j] > 0.f) last_pos = lane * EPT + j;
+        if (e[j] > 0.f) last_pos = tid * SPT + j;
     }
-    below = wave::sum_i32(below);
-    if (below >= len) below = max(wave::max_i32(last_pos), 0);
-    if (lane == 0) {
-        exit_node[kd] = Vn;
-        bonus_token[kd] = c0 + below;
+    below = block_sum_i32(below, s_red);
+    if (below >= len) {
+        const int lp = wave::max_i32(last_pos);
+        if (lane == 0) s_red[wave] = lp;
+        __syncthreads();
+        below = max(max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])), 0);
+    }
+    if (tid == 0) {
+        A.exit_node[kd] = Vn;
+        A.bonus_token[kd] = c0 + below;
     }
 }
 

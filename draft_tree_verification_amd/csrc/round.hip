@@ -43,21 +43,22 @@ __global__ __launch_bounds__(NT) void k_round_attn(AttnArgs a, ReachArgs ra, int
 }
 
 struct CombineArgs {
-    const float *part_o, *part_ml;
+    const uint16_t *part_o;
+    const float *part_ml;
     int splits, Hkv, G, B, Hq;
     size_t rows_all;
     const unsigned *status;
     float *out;
 };
 
-// Launch 3: workgroups [0, R * sbx) draw (request b / sbx, draws 4 (b % sbx)
-// .. + 3), the rest combine the attention splits.
+// Launch 3: workgroups [0, R * n_draws) draw (request b / n_draws, draw
+// b % n_draws), the rest combine the attention splits.
 template <int D, typename T, bool VEC>
 __global__ __launch_bounds__(VOCAB_THREADS) void k_round_tail(SampleArgs<T> sa, int sbx, int n_sample,
                                                             CombineArgs ca) {
     const int b = (int)blockIdx.x;
     if (b < n_sample) {
-        sample_wg<T, VEC>(sa, b % sbx, b / sbx);
+        sample_wg<T, VEC>(sa, b % sbx, b / sbx);   // sbx = draws per request
         return;
     }
     attn_combine_wg<D>(ca.part_o, ca.part_ml, ca.splits, ca.Hkv, ca.G, ca.B, ca.Hq, ca.rows_all,
@@ -80,7 +81,8 @@ void round_attn_nb(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R,
 template <int D, typename T, bool VEC>
 void launch_round_tail(const SampleArgs<T> &sa, int R, int n_draws, const CombineArgs &ca,
                        int n_combine, hipStream_t st) {
-    const int sbx = (n_draws + WAVES_PER_WG - 1) / WAVES_PER_WG;
+    static_assert(SAMPLE_THREADS == VOCAB_THREADS, "draw and combine workgroups share a launch");
+    const int sbx = n_draws;
     const int n_sample = R * sbx;
     k_round_tail<D, T, VEC><<<dim3((unsigned)(n_sample + n_combine)), VOCAB_THREADS, 0, st>>>(
         sa, sbx, n_sample, ca);
@@ -129,7 +131,7 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
     // 2. attention + reach
     const AttnPlan pl = attn_plan(R, B, Hq, Hkv, D, P, RL.reserve);
     const AttnWs AL = attn_ws_layout(R, B, Hq, Hkv, D, P, RL.reserve);
-    float *part_o = (float *)(ws_a + AL.part_o);
+    uint16_t *part_o = (uint16_t *)(ws_a + AL.part_o);
     float *part_ml = (float *)(ws_a + AL.part_ml);
     unsigned *astatus = (unsigned *)(ws_a + AL.status);
     const int n_wg = pl.row_blocks * pl.splits * R * Hkv;

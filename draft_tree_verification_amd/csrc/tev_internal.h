@@ -58,8 +58,8 @@ inline ExitWs exit_ws_layout(int R, int B, int V) {
 
 // Tree-attention workspace:
 //   status  u32 [R]
-//   part_o  f32 [S][R*Hkv][G*B][D]  un-normalised split outputs (S splits)
-//   part_ml f32 [S][R*Hkv][G*B][2]  running max (log2 units) and sum
+//   part_o  f16 [S][R*Hkv][G*B][D]  split outputs o_s / l_s in units of 2^u_s
+//   part_ml f32 [S][R*Hkv][G*B][4]  running max m_s (log2 units), sum l_s, u_s
 struct AttnPlan {
     int nqt, nw;          // query tiles (16 rows) per wave, waves per workgroup
     int rows_per_wg;      // 4 * nqt * 16 (two key groups share the rows)
@@ -86,8 +86,8 @@ inline AttnWs attn_ws_layout(int R, int B, int Hq, int Hkv, int D, int P, int re
     size_t o = 0;
     L.status = o; o = align_up(o + 4 * (size_t)R, 256);
     const size_t S = pl.splits > 1 ? (size_t)pl.splits : 0;
-    L.part_o = o;  o = align_up(o + 4 * S * rows * D, 256);
-    L.part_ml = o; o = align_up(o + 8 * S * rows, 256);
+    L.part_o = o;  o = align_up(o + 2 * S * rows * D, 256);
+    L.part_ml = o; o = align_up(o + 16 * S * rows, 256);
     L.total = o;
     return L;
 }

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(NT) void k_attn_mfma(AttnArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void k_attn_combine(const uint16_t *__restrict__ part_o,
                                                       const float *__restrict__ part_ml,
                                                       int splits, int Hkv, int G, int B, int Hq,
                                                       size_t rows_all,
@@ -124,7 +124,7 @@ hipError_t mfma_impl(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                      float *out, char *ws, const AttnPlan &pl, hipStream_t st) {
     const AttnWs L = attn_ws_layout(R, B, Hq, Hkv, D, P);
     const float c_log2 = (float)((double)scale * 1.4426950408889634);
-    float *part_o = (float *)(ws + L.part_o);
+    uint16_t *part_o = (uint16_t *)(ws + L.part_o);
     float *part_ml = (float *)(ws + L.part_ml);
     unsigned *status = (unsigned *)(ws + L.status);
     const int n_wg = pl.row_blocks * pl.splits * R * Hkv;

@@ -22,6 +22,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 // Plain clang vectors for 16- and 8-byte moves: unlike HIP's uint4 struct they
 // stay in registers (struct copies become memcpy that the compiler keeps in
 // memory).
@@ -89,7 +90,9 @@ struct AttnArgs {
     int B, Hq, Hkv, P;
     float c_log2;
     int row_blocks, splits, keys_per_split, n_wg;
-    float *out, *part_o, *part_ml;
+    float *out;
+    uint16_t *part_o;
+    float *part_ml;
     unsigned *status;
 };
 
@@ -121,7 +124,7 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
     const int row_blocks = A.row_blocks, splits = A.splits, keys_per_split = A.keys_per_split;
     const int n_wg = A.n_wg;
     float *__restrict__ out = A.out;
-    float *__restrict__ part_o = A.part_o;
+    uint16_t *__restrict__ part_o = A.part_o;
     float *__restrict__ part_ml = A.part_ml;
     unsigned *__restrict__ status = A.status;
     constexpr int DS = D / 32;          // k-steps of the score product
@@ -209,18 +212,25 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
             qop[t][ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qp + ds * 32 + grp * 8));
     }
     static_assert(NT >= TEV_MAX_NODES, "one thread per tree node");
-    const int my_par = (last && tid < B) ? parents[(size_t)r * B + tid] : -1;
+    // Unconditional load of a clamped index, stored to LDS below by every
+    // workgroup (a load used only by the last split would be sunk into its
+    // branch, and the compiler would wait for all outstanding loads there).
+    const int par_raw = parents[(size_t)r * B + min(tid, B - 1)];
+    const int my_par = tid < B ? par_raw : -1;
 
+    // Every stage load is unconditional (a workgroup has at least one stage;
+    // loads past the last stage re-read its keys): conditional loads would
+    // make the compiler wait for all outstanding loads where branches join.
     static_assert(PD == 2, "the pipeline below is written out for two register stages");
-    if (0 < nstages) gload(kreg0, vreg0, kbeg);
-    if (1 < nstages) gload(kreg1, vreg1, kbeg + SB);
+    gload(kreg0, vreg0, kbeg);
+    gload(kreg1, vreg1, kbeg + min(1, nstages - 1) * SB);
 
     // Tree contract (parents[0] = -1, 0 <= parents[i] < i) and the ancestor
     // bitmap of every node (bit j of node i: j lies on i's root path).
     bool tree_ok = true;
+    if (tid < TEV_MAX_NODES) s_par[tid] = my_par;   // read by the last split only
     if (last) {
         if (tid == 0) s_bad = 0;
-        if (tid < B) s_par[tid] = my_par;
         __syncthreads();
         if (tid < B && !((tid == 0) ? (my_par == -1) : (my_par >= 0 && my_par < tid))) s_bad = 1;
         __syncthreads();
@@ -338,7 +348,7 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
     };
 
     // Stage 0 into LDS buffer 0 (the tree bitmap above is also published here).
-    if (nstages > 0) lstore(kreg0, vreg0, s_k, s_v);
+    lstore(kreg0, vreg0, s_k, s_v);
     __syncthreads();
 
     // Stage s sits in register slot s % PD until it is written to LDS buffer
@@ -349,7 +359,7 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
     {                                                                                           \
         const int s = s0 + (SL);                                                                \
         if (s < nstages) {                                                                      \
-            if (s + PD < nstages) gload(kreg##SL, vreg##SL, kbeg + (s + PD) * SB);              \
+            gload(kreg##SL, vreg##SL, kbeg + min(s + PD, nstages - 1) * SB);                    \
             const int kb = kbeg + s * SB + kg * KB;                                             \
             if (kb < kend) compute(kb, s & 1, acc, m_run, l_run);                               \
             if (s + 1 < nstages) {                                                              \
@@ -412,14 +422,35 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
                 *reinterpret_cast<f32x4 *>(o + dt * 16 + grp * 4) = val;
             }
         } else {
-            const size_t prow = (size_t)sp * rows_all + (size_t)rg * rows_total + row;
-            float *o = part_o + prow * D;
+            // The split's normalised output o / l in fp16, in units of 2^u
+            // chosen from the row's largest |o / l| (scaled values below 2^15,
+            // the largest above 2^14): half the bytes of fp32 partials, about
+            // 2^-12 relative to the row's largest value.
+            const float inv = 1.0f / lt;
+            float mx = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4 *>(o + dt * 16 + grp * 4) = acc[t][dt];
-            if (grp == 0) {
-                part_ml[prow * 2] = m_run[t];
-                part_ml[prow * 2 + 1] = lt;
+            for (int dt = 0; dt < DT; dt++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) mx = fmaxf(mx, fabsf(acc[t][dt][j]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx *= inv;
+            int ex = 0;
+            (void)frexpf(mx, &ex);                          // mx = f 2^ex, f in [0.5, 1)
+            const int u = (mx > 0.f) ? min(max(ex - 15, -126), 127) : 0;
+            const float sc = inv * __builtin_ldexpf(1.0f, -u);
+            const size_t prow = (size_t)sp * rows_all + (size_t)rg * rows_total + row;
+            uint16_t *o16 = part_o + prow * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) {
+                const f32x4 val = acc[t][dt] * sc;
+                f16x4 h;
+#pragma unroll
+                for (int j = 0; j < 4; j++) h[j] = (_Float16)val[j];
+                *reinterpret_cast<f16x4 *>(o16 + dt * 16 + grp * 4) = h;
             }
+            if (grp == 0)
+                *reinterpret_cast<f32x4 *>(part_ml + prow * 4) = f32x4{m_run[t], lt, (float)u, 0.f};
         }
     }
 }
@@ -427,15 +458,17 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
 constexpr int MAX_SPLITS = 32;
 
 // Merge split partials: one wave per query row (block b of 256 threads takes
-// rows 4b .. 4b + 3); lane s reads split s's (m, l), every lane its D/64 output
-// columns of all splits, all loads issued before the first use.
+// rows 4b .. 4b + 3); lane s reads split s's (m, l, u), every lane its D/64
+// output columns of all splits.  All loads are unconditional (clamped split
+// index), so they are all in flight before the first use.
 template <int D>
-__device__ __forceinline__ void attn_combine_wg(const float *__restrict__ part_o,
+__device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ part_o,
                                                 const float *__restrict__ part_ml, int splits,
                                                 int Hkv, int G, int B, int Hq, size_t rows_all,
                                                 const unsigned *__restrict__ status,
                                                 float *__restrict__ out, const int block) {
     constexpr int DPL = D / 64;
+    static_assert(DPL == 1 || DPL == 2, "head_dim 64 or 128");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const size_t row = (size_t)block * 4 + wave;
     if (row >= rows_all) return;
@@ -444,29 +477,31 @@ __device__ __forceinline__ void attn_combine_wg(const float *__restrict__ part_o
     const int rr = (int)(row - (size_t)rg * rows_total);
     const int r = rg / Hkv, g = rg - r * Hkv;
     const int i = rr / G, hh = rr - i * G;
-    float ms = -kInf, ls = 0.f;
-    if (lane < splits) {
-        ms = part_ml[((size_t)lane * rows_all + row) * 2];
-        ls = part_ml[((size_t)lane * rows_all + row) * 2 + 1];
+    const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + ((size_t)min(lane, splits - 1) * rows_all + row) * 4);
+    uint32_t o[MAX_SPLITS];   // DPL fp16 values of split s (one or two halves)
+#pragma unroll
+    for (int s = 0; s < MAX_SPLITS; s++) {
+        const uint16_t *p = part_o + ((size_t)min(s, splits - 1) * rows_all + row) * D + lane * DPL;
+        o[s] = DPL == 2 ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*p;
     }
-    float o[MAX_SPLITS][DPL];
-#pragma unroll
-    for (int s = 0; s < MAX_SPLITS; s++)
-#pragma unroll
-        for (int j = 0; j < DPL; j++)
-            o[s][j] = (s < splits) ? part_o[((size_t)s * rows_all + row) * D + lane * DPL + j] : 0.f;
+    const bool mine = lane < splits;
+    const float ms = mine ? ml[0] : -kInf, ls = mine ? ml[1] : 0.f;
     const float M = wave::max_f32(ms);
     const float wgt = (ms > -kInf) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
     const float L = wave::sum_f32(ls * wgt);
+    const float f = (wgt * ls) * __builtin_ldexpf(1.0f, mine ? (int)ml[2] : 0);   // weight of split s's unit
     float acc[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; j++) acc[j] = 0.f;
 #pragma unroll
     for (int s = 0; s < MAX_SPLITS; s++) {
         if (s < splits) {
-            const float ws = wave::readlane_f(wgt, s);
+            const float fs = wave::readlane_f(f, s);
 #pragma unroll
-            for (int j = 0; j < DPL; j++) acc[j] = fmaf(ws, o[s][j], acc[j]);
+            for (int j = 0; j < DPL; j++) {
+                const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(o[s] >> (16 * j)));
+                acc[j] = fmaf(fs, (float)h, acc[j]);
+            }
         }
     }
     const bool bad = status[r] != 0u;
