@@ -62,10 +62,10 @@ inline ExitWs exit_ws_layout(int R, int B, int V) {
 //   part_ml f32 [S][R*Hkv][G*B][4]  running max m_s (log2 units), sum l_s, u_s
 struct AttnPlan {
     int nqt, nw;          // query tiles (16 rows) per wave, waves per workgroup
-    int rows_per_wg;      // 4 * nqt * 16 (two key groups share the rows)
+    int rows_per_wg;      // nw * nqt * 16
     int row_blocks;       // ceil(G*B / rows_per_wg)
     int splits;           // prefix splits
-    int keys_per_split;   // multiple of 32 (one block)
+    int keys_per_split;   // multiple of 32
 };
 
 struct AttnWs {

@@ -148,17 +148,19 @@ AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P, int reserve) {
     AttnPlan p{};
     const int G = Hq / Hkv;
     const int rows = G * B;
-    // Query tiles per wave: as many as the rows fill (a workgroup serves
-    // 4 * 16 * nqt rows; two key groups share them).
-    p.nqt = rows > 64 ? 2 : 1;
+    // Query tiles per wave (a workgroup serves 8 waves x 16 nqt rows): two
+    // once the rows fill them, except for a few kv heads of at most 256 rows,
+    // where two row blocks of 128 give more parallelism than more prefix
+    // splits (measured at 1 request, 32/8 heads, B = 64, P = 4096).
+    p.nqt = (rows > NW * 16 && !(rows <= 2 * NW * 16 && (long)R * Hkv < 32)) ? 2 : 1;
     p.nw = NW;
-    p.rows_per_wg = RWV * p.nqt * 16;
+    p.rows_per_wg = NW * p.nqt * 16;
     p.row_blocks = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
     const long base = (long)R * Hkv * p.row_blocks;
     // At most one workgroup per free CU (256 CUs less the reserve), each split
-    // keeping >= 256 prefix keys so that per-split fixed costs stay small.
+    // keeping >= 128 prefix keys so that per-split fixed costs stay small.
     long want = (256 - reserve) / base;
-    long maxs = P / 256;
+    long maxs = P / 128;
     if (maxs < 1) maxs = 1;
     if (maxs > MAX_SPLITS) maxs = MAX_SPLITS;
     int S = (int)(want < maxs ? want : maxs);
@@ -166,7 +168,7 @@ AttnPlan attn_plan(int R, int B, int Hq, int Hkv, int D, int P, int reserve) {
     int kps = 0;
     if (S > 1) {
         kps = (P + S - 1) / S;
-        kps = (kps + KB - 1) / KB * KB;
+        kps = (kps + 31) / 32 * 32;
         S = (P + kps - 1) / kps;
     }
     p.splits = S;

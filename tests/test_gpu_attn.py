@@ -72,3 +72,33 @@ def test_invalid_tree_is_flagged():
     assert flags[1] & tev.TEV_FLAG_TREE and flags[0] == 0
     assert np.all(np.isnan(out[1]))
     assert np.all(np.isfinite(out[0]))
+
+
+RANGE_CASES = ["v_tiny", "v_huge", "v_growing", "v_shrinking", "scores_peaked"]
+
+
+@pytest.mark.parametrize("case", RANGE_CASES)
+def test_value_ranges(case):
+    """V far from unit magnitude, or growing / shrinking by 2^60 across the
+    keys (exercises the kernel's grow-only power-of-two scale of V in fp16),
+    and sharply peaked scores (exercises the lazy reference max)."""
+    GP.log(f"[attn] value range {case}")
+    wl = W.make_custom(case, R=1, B=40, V=300, Hq=8, Hkv=2, D=128, P=700, dtype="bf16",
+                       tree="random", n_uniform=1)
+    nkv = wl.P + wl.B
+    v = W.bf16_bits_to_f32(wl.v).astype(np.float64)
+    ramp = np.arange(nkv) / (nkv - 1) * 60.0 - 30.0          # -30 .. 30 (log2)
+    if case == "v_tiny":
+        v *= 2.0 ** -40
+    elif case == "v_huge":
+        v *= 2.0 ** 40
+    elif case == "v_growing":
+        v *= (2.0 ** ramp)[None, None, :, None]
+    elif case == "v_shrinking":
+        v *= (2.0 ** -ramp)[None, None, :, None]
+    elif case == "scores_peaked":
+        q = W.bf16_bits_to_f32(wl.q).astype(np.float64) * 8.0
+        wl.q = W.f32_to_bf16_bits(q.astype(np.float32))
+    wl.v = W.f32_to_bf16_bits(v.astype(np.float32))
+    err = GP.check_attn(wl)
+    GP.log(f"[attn] {case} ok max row error {err:.3e}")
