@@ -7,12 +7,13 @@
 //   P(0) = 1, P(u) = P(pa(u)) p_pa(u)(x_u),  w = P rho,  C = sum_{u>0} P(u),
 //   V = inverse CDF of w at u1,  Y = inverse CDF of p_V^res at u2.
 //
-// k_vocab -- grid (ceil(nc / 4), R*B), 4 independent waves per workgroup,
-// each wave on its own 4096-token chunk of one logit row, no workgroup
-// barrier: the chunk maximum, then the chunk's sum of 2^(l*sL - M_c) split
-// into a residual part (non-child tokens, masked through a per-wave LDS bitmap
-// of the row's child tokens) and a child part.  Each logit is read exactly
-// once: this pass is HBM-bound.
+// k_vocab -- grid (ceil(nc / (4 / SPLIT)), R*B), 4 waves per workgroup, one
+// 4096-token chunk of one logit row per SPLIT waves (SPLIT = 2 for small
+// problems, where halving the work per wave evens out the last round of waves
+// over the SIMDs): the chunk maximum, then the chunk's sum of 2^(l*sL - M_c)
+// split into a residual part (non-child tokens, masked through a per-wave LDS
+// bitmap of the row's child tokens) and a child part.  Each logit is read
+// exactly once: this pass is HBM-bound.
 //
 // k_reach -- one workgroup of 1024 threads per request:
 //   row pass (16 waves, rows dealt round-robin, a batch of four rows' chunk
@@ -47,78 +48,121 @@ namespace tev {
 namespace {
 
 // ----------------------------------------------------------------------------
-// k_vocab.  Chunk c of row rv: lane t holds the elements k*(64*VW) + t*VW + j
-// (coalesced 16-byte vectors); the row's child tokens inside the chunk are
-// marked in a per-wave LDS bitmap whose word t belongs to lane t.
+// k_vocab.  Workgroup (x, rv): 4 / SPLIT consecutive chunks of row rv, SPLIT
+// waves per chunk, wave h of a chunk on its part [h * TPW, h * TPW + TPW),
+// TPW = 4096 / SPLIT tokens: lane t holds the part's elements
+// k*(64*VW) + t*VW + j (coalesced 16-byte vectors).  With two waves per chunk
+// (small problems: finer balance over the SIMDs) the pair agrees on the
+// chunk's offset M_c through LDS (one barrier), sums its halves against it,
+// and the first wave writes the chunk's partials (second barrier); with one
+// wave per chunk no barrier is involved.  The row's child tokens inside a part
+// are marked in a per-wave LDS bitmap whose word t belongs to lane t (EPW
+// bits per lane).  Parts shorter than TPW tokens (the row's tail) take a
+// masked path; the rest run without any per-element test.
 // ----------------------------------------------------------------------------
-template <typename T, bool VEC>
+template <typename T, bool VEC, int NPLV, int SPLIT>
 __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
     const T *__restrict__ logits, const int32_t *__restrict__ parents,
     const int32_t *__restrict__ tokens, int B, int V, int nc, float sL, ExitPtrs W) {
+    constexpr int TPW = CHUNK / SPLIT;  // tokens per wave
+    constexpr int EPW = TPW / 64;       // elements per lane
+    constexpr int MW = EPW / 32;        // 32-bit child-mask words per lane
     constexpr int VW = 16 / (int)sizeof(T);
-    constexpr int NV = EPT / VW;
+    constexpr int NV = EPW / VW;        // 16-byte vectors per lane
     constexpr int SPAN = 64 * VW;
     constexpr unsigned VMASK = (1u << VW) - 1u;
+    static_assert(SPLIT == 1 || SPLIT == 2, "one or two waves per chunk");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int c = blockIdx.x * WAVES_PER_WG + wave;
+    const int c = blockIdx.x * (WAVES_PER_WG / SPLIT) + wave / SPLIT;
+    const int h = wave % SPLIT;
     const int rv = blockIdx.y;
     const int r = rv / B, v = rv - r * B;
-    __shared__ unsigned s_mask[WAVES_PER_WG][128];
-    if (c >= nc) return;
+    __shared__ unsigned s_mask[WAVES_PER_WG][64 * MW];
+    __shared__ float s_max[WAVES_PER_WG];
+    __shared__ double s_sum[WAVES_PER_WG][2];
+    __shared__ unsigned s_flag[WAVES_PER_WG];
+    const bool live = c < nc;          // uniform per wave; both waves of a chunk agree
     const int c0 = c * CHUNK;
-    const int len = min(CHUNK, V - c0);
+    const int h0 = c0 + h * TPW;
+    const int len = live ? min(TPW, V - h0) : 0;   // <= 0: an empty half of the tail chunk
     const int32_t *par = parents + (size_t)r * B;
     const int32_t *tok = tokens + (size_t)r * B;
 
     // The tree arrays first (a few hundred bytes, cache-resident after the
     // first waves): the child mask below is then built while the logits are
     // still in flight.  Unconditional loads of clamped indices.
-    int cpar[NPL], ctok[NPL];
+    int cpar[NPLV], ctok[NPLV];
 #pragma unroll
-    for (int k = 0; k < NPL; k++) {
+    for (int k = 0; k < NPLV; k++) {
         const int uc = min(1 + lane + 64 * k, B - 1);
         cpar[k] = par[uc];
         ctok[k] = tok[uc];
     }
-    const T *row = logits + (size_t)rv * (size_t)V + c0;
-    float x[EPT];
-    load_chunk<T, VEC>(row, len, lane, x);
-    s_mask[wave][2 * lane] = 0u;
-    s_mask[wave][2 * lane + 1] = 0u;
+    const T *row = logits + (size_t)rv * (size_t)V + h0;
+    float x[EPW];
+    const bool full = len == TPW;
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < NV; k++) {
+            const int idx = k * SPAN + lane * VW;
+            if (VEC) {
+                load16(row + idx, &x[k * VW]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VW; j++) x[k * VW + j] = to_f32<T>(row[idx + j]);
+            }
+        }
+    } else if (len > 0) {
+        load_chunk_part<T, VEC, EPW>(row, len, lane, x);
+    } else {
+#pragma unroll
+        for (int j = 0; j < EPW; j++) x[j] = -kInf;
+    }
+#pragma unroll
+    for (int q = 0; q < MW; q++) s_mask[wave][MW * lane + q] = 0u;
     wave::lds_sync();
     bool dup = false;
-    int mine_o[NPL];   // chunk offset of child 1 + lane + 64 k, or -1
+    int mine_o[NPLV];   // half offset of child 1 + lane + 64 k, or -1
 #pragma unroll
-    for (int k = 0; k < NPL; k++) {
+    for (int k = 0; k < NPLV; k++) {
         // the test is evaluated outside the branch, so that the tree loads
         // cannot sink into it (a load inside the branch would wait for the
         // logits too)
-        const int o = ctok[k] - c0;
+        const int o = ctok[k] - h0;
         const bool hit = (1 + lane + 64 * k < B) & (cpar[k] == v) & (o >= 0) & (o < len);
         mine_o[k] = hit ? o : -1;
         if (hit) {
             const int kk = o / SPAN, rem = o - kk * SPAN;
-            const int bitpos = kk * VW + (rem % VW);           // 0..63 within the owner lane
+            const int bitpos = kk * VW + (rem % VW);           // 0..EPW-1 within the owner lane
             const unsigned bit = 1u << (bitpos & 31);
-            const unsigned old = atomicOr(&s_mask[wave][2 * (rem / VW) + (bitpos >> 5)], bit);
+            const unsigned old = atomicOr(&s_mask[wave][MW * (rem / VW) + (bitpos >> 5)], bit);
             dup |= (old & bit) != 0u;
         }
     }
     wave::lds_sync();
-    const uint64_t mybits = (uint64_t)s_mask[wave][2 * lane] | ((uint64_t)s_mask[wave][2 * lane + 1] << 32);
+    uint64_t mybits = s_mask[wave][MW * lane];
+    if (MW == 2) mybits |= (uint64_t)s_mask[wave][MW * lane + MW - 1] << 32;
     const bool wave_has_children = __any(mybits != 0ull);
 
+    // chunk maximum: this half's, then the pair's through LDS
     float m = x[0];
 #pragma unroll
-    for (int j = 1; j < EPT; j++) m = fmaxf(m, x[j]);
+    for (int j = 1; j + 1 < EPW; j += 2) m = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, x[j]), x[j + 1]);
+    m = __builtin_elementwise_maximum(m, x[EPW - 1]);
     m = wave::max_f32(m);
+    float mc = m;
+    if (SPLIT == 2) {
+        if (lane == 0) s_max[wave] = m;
+        __syncthreads();
+        mc = __builtin_elementwise_maximum(s_max[wave & ~1], s_max[wave | 1]);
+    }
     // Integer offset: every term is below 2, and rescaling between chunk
     // offsets is an exact power of two.
-    const float Mc = floorf(m * sL);
+    const float Mc = floorf(mc * sL);
     double accR = 0.0, accC = 0.0;
-    if (m > -kInf) {
+    if (mc > -kInf) {
         if (!wave_has_children) {
-            // common case: no child token of v in this chunk
+            // common case: no child token of v in this half
 #pragma unroll
             for (int k = 0; k < NV; k++) {
                 float e[VW];
@@ -153,31 +197,46 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
             }
         }
     }
-    const double Rc = wave::sum_f64(accR);
-    const double Cc = wave::sum_f64(accC);
+    const double Rh = wave::sum_f64(accR);
+    const double Ch = wave::sum_f64(accC);
     const bool any_dup = __any(dup);
-    if (lane == 0) {
-        const size_t o = (size_t)rv * nc + c;
-        unsigned f = 0u;
-        if (!(m == m) || m == kInf || isnan(Rc) || isnan(Cc)) f |= TEV_FLAG_NONFINITE;
-        if (any_dup) f |= TEV_FLAG_TREE;
-        W.flags[o] = f;
-        W.part_m[o] = (m > -kInf) ? Mc : -kInf;
-        W.part_r[o] = Rc;
-        W.part_c[o] = Cc;
+    unsigned f = 0u;
+    if (!(m == m) || m == kInf || isnan(Rh) || isnan(Ch)) f |= TEV_FLAG_NONFINITE;
+    if (any_dup) f |= TEV_FLAG_TREE;
+    if (SPLIT == 1) {
+        if (lane == 0 && live) {
+            const size_t o = (size_t)rv * nc + c;
+            W.flags[o] = f;
+            W.part_m[o] = (mc > -kInf) ? Mc : -kInf;
+            W.part_r[o] = Rh;
+            W.part_c[o] = Ch;
+        }
+    } else if (lane == 0) {
+        s_sum[wave][0] = Rh;
+        s_sum[wave][1] = Ch;
+        s_flag[wave] = f;
     }
-    // Each child token of v lies in exactly one chunk of v's row: that chunk
+    // Each child token of v lies in exactly one part of v's row: that part
     // records the child's own term (the same f32 operations as the sums) and
     // the chunk offset, so the reach needs no gather of its own.
     if (wave_has_children) {
 #pragma unroll
-        for (int k = 0; k < NPL; k++) {
+        for (int k = 0; k < NPLV; k++) {
             if (mine_o[k] >= 0) {
                 const float xl = to_f32<T>(row[mine_o[k]]);
-                const float t = (m > -kInf) ? __builtin_amdgcn_exp2f(fmaf(xl, sL, -Mc)) : 0.f;
+                const float t = (mc > -kInf) ? __builtin_amdgcn_exp2f(fmaf(xl, sL, -Mc)) : 0.f;
                 W.cterm[(size_t)r * B + 1 + lane + 64 * k] = make_float2(t, Mc);
             }
         }
+    }
+    if (SPLIT == 1) return;
+    __syncthreads();
+    if (h == 0 && lane == 0 && live) {
+        const size_t o = (size_t)rv * nc + c;
+        W.flags[o] = s_flag[wave] | s_flag[wave + 1];
+        W.part_m[o] = (mc > -kInf) ? Mc : -kInf;
+        W.part_r[o] = s_sum[wave][0] + s_sum[wave + 1][0];
+        W.part_c[o] = s_sum[wave][1] + s_sum[wave + 1][1];
     }
 }
 
@@ -243,8 +302,19 @@ template <typename T, bool VEC>
 void vocab_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R, int B,
                 int V, float sL, char *ws, hipStream_t st) {
     const int nc = n_chunks(V);
-    k_vocab<T, VEC><<<dim3((nc + WAVES_PER_WG - 1) / WAVES_PER_WG, R * B), VOCAB_THREADS, 0, st>>>(
-        logits, parents, tokens, B, V, nc, sL, exit_ptrs(ws, R, B, V));
+    const ExitPtrs W = exit_ptrs(ws, R, B, V);
+    // Two waves per chunk while the chunks alone would leave the SIMDs with a
+    // few waves each (an uneven last round), one wave per chunk otherwise.
+    const bool split = (long)R * B * nc < 4L * 1024;
+#define TEV_VOCAB(NP, SP)                                                                          \
+    k_vocab<T, VEC, NP, SP><<<dim3((nc + WAVES_PER_WG / SP - 1) / (WAVES_PER_WG / SP), R * B),     \
+                              VOCAB_THREADS, 0, st>>>(logits, parents, tokens, B, V, nc, sL, W)
+    if (B <= 65) {
+        if (split) TEV_VOCAB(1, 2); else TEV_VOCAB(1, 1);
+    } else {
+        if (split) TEV_VOCAB(NPL, 2); else TEV_VOCAB(NPL, 1);
+    }
+#undef TEV_VOCAB
 }
 
 void reach_impl(const int32_t *parents, const int32_t *tokens, int R, int B, int V, float sL,

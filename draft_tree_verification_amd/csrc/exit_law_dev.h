@@ -8,12 +8,13 @@
 //   P(0) = 1, P(u) = P(pa(u)) p_pa(u)(x_u),  w = P rho,  C = sum_{u>0} P(u),
 //   V = inverse CDF of w at u1,  Y = inverse CDF of p_V^res at u2.
 //
-// k_vocab -- grid (ceil(nc / 4), R*B), 4 independent waves per workgroup,
-// each wave on its own 4096-token chunk of one logit row, no workgroup
-// barrier: the chunk maximum, then the chunk's sum of 2^(l*sL - M_c) split
-// into a residual part (non-child tokens, masked through a per-wave LDS bitmap
-// of the row's child tokens) and a child part.  Each logit is read exactly
-// once: this pass is HBM-bound.
+// k_vocab -- grid (ceil(nc / (4 / SPLIT)), R*B), 4 waves per workgroup, one
+// 4096-token chunk of one logit row per SPLIT waves (SPLIT = 2 for small
+// problems, where halving the work per wave evens out the last round of waves
+// over the SIMDs): the chunk maximum, then the chunk's sum of 2^(l*sL - M_c)
+// split into a residual part (non-child tokens, masked through a per-wave LDS
+// bitmap of the row's child tokens) and a child part.  Each logit is read
+// exactly once: this pass is HBM-bound.
 //
 // k_reach -- one workgroup of 1024 threads per request:
 //   row pass (16 waves, rows dealt round-robin, a batch of four rows' chunk
@@ -366,6 +367,31 @@ __device__ __forceinline__ void load_chunk(const T *chunk, int len, int lane, fl
         const int idx = k * SPAN + lane * VW;
         if (VEC) {
             // len is a multiple of VW here (16-byte rows), so len - VW is a valid vector
+            load16(chunk + min(idx, len - VW), &x[k * VW]);
+#pragma unroll
+            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
+        } else {
+#pragma unroll
+            for (int j = 0; j < VW; j++) {
+                const float t = to_f32<T>(chunk[min(idx + j, len - 1)]);
+                x[k * VW + j] = (idx + j < len) ? t : -kInf;
+            }
+        }
+    }
+}
+
+// A partial half (1 <= len < N * ... tokens) with the interleaved ownership of
+// the vocabulary pass: N elements per lane, element k*(64*VW) + lane*VW + j;
+// out-of-range elements become -inf.  Loads are unconditional, of clamped
+// valid addresses (len >= VW when VEC: 16-byte rows).
+template <typename T, bool VEC, int N>
+__device__ __forceinline__ void load_chunk_part(const T *chunk, int len, int lane, float *x) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    constexpr int SPAN = 64 * VW;
+#pragma unroll
+    for (int k = 0; k < N / VW; k++) {
+        const int idx = k * SPAN + lane * VW;
+        if (VEC) {
             load16(chunk + min(idx, len - VW), &x[k * VW]);
 #pragma unroll
             for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
