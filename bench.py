@@ -136,6 +136,51 @@ def load_traffic(config: str, src_hash: str):
     return t
 
 
+COPY_BYTES = 512 << 20   # calibration copy for the HBM byte counters
+
+
+def summarize_counters(config: str, fetch_db: str, write_db: str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel of a
+    --counters run, scaled by what the same counter reads for the calibration
+    copy (COPY_BYTES read and COPY_BYTES written), into
+    profiles/traffic_<config>.json, tagged with the kernel source hash."""
+    import sqlite3
+    from collections import defaultdict
+
+    def per_kernel(db, counter):
+        con = sqlite3.connect(db)
+        rows = con.execute("select kernel_name, dispatch_id, value from counters_collection "
+                           "where counter_name = ?", (counter,)).fetchall()
+        acc = defaultdict(lambda: defaultdict(float))
+        for name, disp, val in rows:
+            acc[name][disp] += val
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}, \
+               {k: max(v.values()) for k, v in acc.items()}
+
+    fetch, fetch_max = per_kernel(fetch_db, "FETCH_SIZE")
+    write, write_max = per_kernel(write_db, "WRITE_SIZE")
+    copy_k = max((k for k in fetch_max if "copy" in k.lower()), key=lambda k: fetch_max[k])
+    f_fetch = COPY_BYTES / (fetch_max[copy_k] * 1024.0)
+    f_write = COPY_BYTES / (write_max[copy_k] * 1024.0)
+    short = lambda k: k.replace("void ", "").replace("tev::(anonymous namespace)::", "").split("(")[0].split("<")[0]
+    out = {"kernel_source_hash": kernel_source_hash(), "workload": config,
+           "calibration": {"kernel": short(copy_k), "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                           "fetch_kib": fetch_max[copy_k], "write_kib": write_max[copy_k],
+                           "fetch_factor": f_fetch, "write_factor": f_write},
+           "kernels": {}}
+    for k in fetch:
+        if not short(k).startswith("k_"):
+            continue
+        fb = fetch[k] * 1024.0 * f_fetch
+        wb = write.get(k, 0.0) * 1024.0 * f_write
+        out["kernels"][short(k)] = {"fetch_kib": fetch[k], "write_kib": write.get(k), "fetch_bytes": fb,
+                                    "write_bytes": wb, "bytes_per_launch": fb + wb}
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,9 +194,19 @@ def main():
     ap.add_argument("--call-iters", type=int, default=100)
     ap.add_argument("--rounds-per-graph", type=int, default=11,
                     help="rounds captured back to back in one graph for the timed loop")
+    ap.add_argument("--counters", type=int, default=0,
+                    help="counter-collection mode: replay this many one-round graphs and one "
+                         "calibration copy of a known size, then exit (run under rocprofv3 --pmc)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "databases (FETCH_SIZE run, WRITE_SIZE run) of a --counters run")
     ap.add_argument("--separate", action="store_true",
                     help="time the three calls tev_tree_attn, tev_exit_law, tev_sample instead of tev_verify_round")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.config, *args.summarize_counters)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verification stage "
@@ -242,6 +297,17 @@ def main():
         return graphs
 
     g_step = capture(step)
+    if args.counters:
+        with torch.cuda.stream(stream):
+            for i in range(args.counters):
+                g_step[i % ring].replay()
+            # calibration: a device copy of exactly COPY_BYTES (read once, written once)
+            src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] counters run: {args.counters} rounds and one {COPY_BYTES >> 20} MiB copy")
+        return
     # Graphs of G consecutive rounds (distinct ring slots): as nodes of a
     # captured decode step would run them, without one graph launch per round.
     G = max(1, min(args.rounds_per_graph, ring))
@@ -359,7 +425,8 @@ def main():
     roof["launch_us"] = round(phase_us[dominant], 3)
     src_hash = kernel_source_hash()
     traffic = load_traffic(wl.name, src_hash)
-    roof["traffic"] = traffic.get(dominant, {}).get("bytes_per_launch") if traffic else None
+    tk = traffic.get("kernels", {}).get(dominant) if traffic else None
+    roof["traffic"] = round(tk["bytes_per_launch"]) if tk else None
 
     cpu = None
     if not args.no_cpu_baseline:
