@@ -64,11 +64,12 @@ def _load():
         lib.oracle_exit_law.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, vp, vp, vp, ip]
         lib.oracle_sample.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, ip, vp, vp, vp, ip]
         lib.oracle_residual_cdf.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp]
+        lib.oracle_predraw.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, ip, vp, vp, vp, vp, ip]
         lib.oracle_tree_attn.argtypes = [vp, vp, vp, ip, vp, ip, ip, ip, ip, ip, ip, dp, vp, vp,
                                          ctypes.c_int64, ip]
         lib.oracle_check_tree.argtypes = [vp, vp, ip, ip]
         lib.oracle_max_threads.argtypes = [ip]
-        for f in ("oracle_exit_law", "oracle_sample", "oracle_residual_cdf", "oracle_tree_attn",
+        for f in ("oracle_exit_law", "oracle_sample", "oracle_residual_cdf", "oracle_predraw", "oracle_tree_attn",
                   "oracle_check_tree", "oracle_max_threads"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -163,6 +164,38 @@ def sample(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarr
     if st != 0:
         raise OracleError(f"oracle_sample failed with status {st}")
     return Draws(en, bt, band[..., 0].astype(bool), band[..., 1].astype(bool))
+
+
+@dataclass
+class PredrawDraws:
+    node_draw: np.ndarray    # [R][n][B] int32: R_v of every node
+    exit_node: np.ndarray    # [R][n] int32
+    bonus_token: np.ndarray  # [R][n] int32
+    band: np.ndarray         # [R][n] bool: a draw on the walked path within 1e-6 of a boundary
+
+
+def predraw(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
+            uniforms: np.ndarray, inv_temperature: float = 1.0, nthreads: int = 0) -> PredrawDraws:
+    """Predraw-and-follow verification (2610.11750 App. A.4.1): one draw per
+    node from its full target row, then the walk from the root.
+    uniforms [R][n][B] (one per node per draw)."""
+    lg = _as_input(logits, dtype)
+    if lg.ndim == 2:
+        lg = lg[None]
+    R, B, V = lg.shape
+    par = np.ascontiguousarray(parents, dtype=np.int32).reshape(R, B)
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(R, B)
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(R, -1, B)
+    n = u.shape[1]
+    nd = np.empty((R, n, B), np.int32)
+    en = np.empty((R, n), np.int32); bt = np.empty((R, n), np.int32)
+    band = np.empty((R, n), np.uint8)
+    st = _load().oracle_predraw(_ptr(lg), _DTYPE_CODES[dtype], _ptr(par), _ptr(tok), R, B, V,
+                                float(inv_temperature), _ptr(u), n, _ptr(nd), _ptr(en), _ptr(bt),
+                                _ptr(band), int(nthreads))
+    if st != 0:
+        raise OracleError(f"oracle_predraw failed with status {st}")
+    return PredrawDraws(nd, en, bt, band.astype(bool))
 
 
 def residual_cdf(logits_req: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,

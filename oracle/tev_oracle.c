@@ -325,6 +325,80 @@ int oracle_sample(const void *logits, int dtype, const int32_t *parents, const i
 }
 
 /*
+ * Predraw-and-follow verification (2610.11750 App. A.4.1), the baseline the
+ * pages measure TEV against.  Before any test, every node v draws its own
+ * token R_v from its full target row p_v (Eq. 1), children included.  The
+ * walk starts at the root; at node v it moves to the child whose incoming
+ * token equals R_v (sibling tokens are distinct, so at most one does) and
+ * otherwise stops there: the exit node is v and the bonus token is R_v.
+ *   uniforms  [R][n][B]  u for node v's draw of draw n
+ * Outputs: node_draw [R][n][B] (R_v, the inverse CDF of p_v in token order at
+ * u), exit_node and bonus_token [R][n]; band [R][n] = 1 when the draw of any
+ * node on the walked path lies within 1e-6 of a boundary of its bin (the
+ * draws of nodes off the path cannot change the outcome).
+ * Rows are processed one request at a time: B cumulative rows of V doubles.
+ */
+int oracle_predraw(const void *logits, int dtype, const int32_t *parents, const int32_t *tokens,
+                   int R, int B, int V, double inv_temperature, const float *uniforms,
+                   int n_draws, int32_t *node_draw, int32_t *exit_node, int32_t *bonus_token,
+                   unsigned char *band, int nthreads) {
+    if (R < 1 || B < 1 || V < 1 || n_draws < 1 || !(inv_temperature > 0.0)) return 3;
+    set_threads(nthreads);
+    for (int r = 0; r < R; r++)
+        if (oracle_check_tree(parents + (size_t)r * B, tokens + (size_t)r * B, B, V)) return 1;
+    double *cum = (double *)malloc(sizeof(double) * (size_t)B * (size_t)V);
+    unsigned char *nb = (unsigned char *)malloc((size_t)n_draws * (size_t)B);
+    if (!cum || !nb) { free(cum); free(nb); return 4; }
+    int status = 0;
+    for (int r = 0; r < R && status == 0; r++) {
+        const int32_t *par = parents + (size_t)r * B;
+        const int32_t *tok = tokens + (size_t)r * B;
+        size_t row0 = (size_t)r * B * V;
+        /* running sums of exp(s x_a - m_v) in token order, one row per node */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int v = 0; v < B; v++) {
+            double m, Z;
+            int st = row_softmax_parts(logits, dtype, row0 + (size_t)v * V, V, inv_temperature, &m, &Z);
+            if (st) {
+#pragma omp critical
+                status = st;
+                continue;
+            }
+            double run = 0.0;
+            for (int a = 0; a < V; a++) {
+                run += exp(inv_temperature * widen(logits, dtype, row0 + (size_t)v * V + a) - m);
+                cum[(size_t)v * V + a] = run;
+            }
+        }
+        if (status) break;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int n = 0; n < n_draws; n++) {
+            size_t k = (size_t)r * n_draws + n;
+            for (int v = 0; v < B; v++)
+                node_draw[k * B + v] = inverse_cdf(cum + (size_t)v * V, V,
+                                                   (double)uniforms[k * B + v], &nb[(size_t)n * B + v]);
+            int v = 0;
+            unsigned char on_band = 0;
+            for (;;) {
+                int d = node_draw[k * B + v];
+                on_band |= nb[(size_t)n * B + v];
+                int next = -1;
+                for (int u = v + 1; u < B; u++)
+                    if (par[u] == v && tok[u] == d) { next = u; break; }
+                if (next < 0) break;
+                v = next;
+            }
+            exit_node[k] = v;
+            bonus_token[k] = node_draw[k * B + v];
+            band[k] = on_band;
+        }
+    }
+    free(cum);
+    free(nb);
+    return status;
+}
+
+/*
  * One layer of ancestor-masked tree attention (2610.00321 App. B Lemma 1;
  * App. C "Packed verification"; App. F varlen verifier).
  *   q   [R][B][Hq][D];  k, v [R][Hkv][P + B][D]  (cache row P + i is node i)
