@@ -298,6 +298,157 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_residual_cdf(
     }
 }
 
+// ----------------------------------------------------------------------------
+// Predraw-and-follow verification ("Where Draft Trees Lose Target Mass",
+// App. A.4.1): every node draws R_v from its full target row p_v (children
+// included), then the walk from the root follows the child whose token is
+// R_v and stops where none is; the exit node is that node, the bonus token its
+// draw.  The rows' chunk partials of the vocabulary pass serve the draws, so a
+// node draw reads its row's chunk sums and one chunk.
+//
+// k_predraw_nodes -- grid (ceil(B / 4), n_draws, R), one wave per node draw:
+//   the chunk of the draw from the running sums of (residual + child) chunk
+//   sums at the row offset, then an fp64 scan of that chunk's terms (the same
+//   f32 terms as the vocabulary pass) in token order.
+// k_predraw_walk -- grid (ceil(n_draws / 4), R), one wave per draw: the walk,
+//   one ballot over the tree per step (at most B steps).
+// ----------------------------------------------------------------------------
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void k_predraw_nodes(
+    const T *__restrict__ logits, int B, int V, int nc, float sL, const unsigned *__restrict__ status,
+    const float *__restrict__ part_m, const double *__restrict__ part_r,
+    const double *__restrict__ part_c, const float *__restrict__ row_m,
+    const float *__restrict__ uniforms, int n_draws, int32_t *__restrict__ node_draw) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int v = blockIdx.x * 4 + wave;
+    const int d = blockIdx.y, r = blockIdx.z;
+    if (v >= B) return;
+    const size_t k = ((size_t)r * n_draws + d) * B + v;
+    const size_t rb = (size_t)r * B + v;
+    const unsigned st = status[r];
+    const double u = (double)uniforms[k];
+    const float Mv = row_m[rb];
+    if (st != 0u) {
+        if (lane == 0) node_draw[k] = -1;
+        return;
+    }
+    // running sums of the full row's chunk sums, in units of 2^-M_v
+    auto chunk_sum = [&](int c) -> double {
+        const int cl = min(c, nc - 1);
+        const float mc = part_m[rb * nc + cl];
+        const double fs = (part_r[rb * nc + cl] + part_c[rb * nc + cl]) * ((mc > -kInf) ? pow2_int(mc - Mv) : 0.0);
+        return c < nc ? fs : 0.0;
+    };
+    double total = 0.0;
+    for (int c0 = 0; c0 < nc; c0 += 64) total += wave::sum_f64(chunk_sum(c0 + lane));
+    const double t = u * total;
+    // chunk: the smallest c with t < W_c (W the running sums)
+    int cc = 0;
+    double carry = 0.0;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const double fs = chunk_sum(c0 + lane);
+        const double incl = carry + wave::incl_scan_f64(fs, lane);
+        cc += wave::sum_i32((c0 + lane < nc && incl <= t) ? 1 : 0);
+        carry = wave::readlane_d(incl, 63);
+    }
+    if (cc >= nc) {   // rounding left no bin: the last chunk with positive mass
+        int best = -1;
+        for (int c = lane; c < nc; c += 64)
+            if (chunk_sum(c) > 0.0) best = max(best, c);
+        cc = max(wave::max_i32(best), 0);
+    }
+    double before = 0.0;
+    for (int c0 = 0; c0 < cc; c0 += 64) {
+        const int c = c0 + lane;
+        before += wave::sum_f64(c < cc ? chunk_sum(c) : 0.0);
+    }
+    const int c0 = cc * CHUNK;
+    const int len = min(CHUNK, V - c0);
+    const float Mc = part_m[rb * nc + cc];
+    // offsets are integers with Mc <= Mv: the rescale is an exact power of two
+    const double target = __builtin_ldexp(t - before, (int)fminf(Mv - Mc, 2000.f));
+    float x[EPT];
+    segment_load<T, VEC>(logits + rb * (size_t)V + c0, len, lane, x);
+    float e[EPT];
+    segment_terms(x, sL, Mc, 0ull, e);
+    double seg = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPT; j++) seg += (double)e[j];
+    double run = wave::incl_scan_f64(seg, lane) - seg;
+    int below = 0, last_pos = -1;
+#pragma unroll
+    for (int j = 0; j < EPT; j++) {
+        run += (double)e[j];
+        below += (run <= target) ? 1 : 0;
+        if (e[j] > 0.f) last_pos = lane * EPT + j;
+    }
+    below = wave::sum_i32(below);
+    if (below >= len) below = max(wave::max_i32(last_pos), 0);
+    if (lane == 0) node_draw[k] = c0 + below;
+}
+
+__global__ __launch_bounds__(256) void k_predraw_walk(
+    const int32_t *__restrict__ parents, const int32_t *__restrict__ tokens, int B,
+    const unsigned *__restrict__ status, const int32_t *__restrict__ node_draw, int n_draws,
+    int32_t *__restrict__ exit_node, int32_t *__restrict__ bonus_token) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int d = blockIdx.x * 4 + wave, r = blockIdx.y;
+    if (d >= n_draws) return;
+    const size_t kd = (size_t)r * n_draws + d;
+    const int32_t *nd = node_draw + kd * B;
+    int cp[NPL], ct[NPL], dr[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; q++) {
+        const int uq = min(lane + 64 * q, B - 1);
+        cp[q] = parents[(size_t)r * B + uq];
+        ct[q] = tokens[(size_t)r * B + uq];
+        dr[q] = nd[uq];
+    }
+    if (status[r] != 0u) {
+        if (lane == 0) { exit_node[kd] = -1; bonus_token[kd] = -1; }
+        return;
+    }
+    int v = 0, dv = -1;
+    for (int step = 0; step < B; step++) {   // a walk visits at most B nodes
+        const int q = v >> 6;                 // uniform
+        int val = dr[0];
+#pragma unroll
+        for (int qq = 1; qq < NPL; qq++) val = (q == qq) ? dr[qq] : val;
+        dv = __builtin_amdgcn_readlane(val, v & 63);
+        int next = -1;
+#pragma unroll
+        for (int qq = 0; qq < NPL; qq++) {
+            const int uq = lane + 64 * qq;
+            const bool hit = (uq < B) & (uq > 0) & (cp[qq] == v) & (ct[qq] == dv);
+            const unsigned long long bal = __ballot(hit);
+            if (next < 0 && bal != 0ull) next = 64 * qq + (int)__builtin_ctzll(bal);
+        }
+        if (next < 0) break;
+        v = next;
+    }
+    if (lane == 0) {
+        exit_node[kd] = v;
+        bonus_token[kd] = dv;
+    }
+}
+
+template <typename T, bool VEC>
+hipError_t predraw_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R,
+                        int B, int V, float sL, const char *ws, const float *uniforms,
+                        int n_draws, int32_t *node_draw, int32_t *exit_node, int32_t *bonus,
+                        hipStream_t st) {
+    const ExitWs L = exit_ws_layout(R, B, V);
+    const int nc = n_chunks(V);
+    const unsigned *status = (const unsigned *)(ws + L.status);
+    k_predraw_nodes<T, VEC><<<dim3((B + 3) / 4, n_draws, R), 256, 0, st>>>(
+        logits, B, V, nc, sL, status, (const float *)(ws + L.part_m),
+        (const double *)(ws + L.part_r), (const double *)(ws + L.part_c),
+        (const float *)(ws + L.row_m), uniforms, n_draws, node_draw);
+    k_predraw_walk<<<dim3((n_draws + 3) / 4, R), 256, 0, st>>>(parents, tokens, B, status, node_draw,
+                                                                  n_draws, exit_node, bonus);
+    return hipGetLastError();
+}
+
 template <typename T, bool VEC>
 void vocab_impl(const T *logits, const int32_t *parents, const int32_t *tokens, int R, int B,
                 int V, float sL, char *ws, hipStream_t st) {
@@ -390,6 +541,20 @@ hipError_t launch_sample(const void *logits, int dtype, bool vec, const int32_t 
     const float *p = (const float *)logits;
     return vec ? sample_impl<float, true>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, exit_node, bonus_token, st)
                : sample_impl<float, false>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, exit_node, bonus_token, st);
+}
+
+hipError_t launch_predraw(const void *logits, int dtype, bool vec, const int32_t *parents,
+                          const int32_t *tokens, int R, int B, int V, float sL, const char *ws,
+                          const float *uniforms, int n_draws, int32_t *node_draw,
+                          int32_t *exit_node, int32_t *bonus_token, hipStream_t st) {
+    if (dtype == TEV_BF16) {
+        const uint16_t *p = (const uint16_t *)logits;
+        return vec ? predraw_impl<uint16_t, true>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, node_draw, exit_node, bonus_token, st)
+                   : predraw_impl<uint16_t, false>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, node_draw, exit_node, bonus_token, st);
+    }
+    const float *p = (const float *)logits;
+    return vec ? predraw_impl<float, true>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, node_draw, exit_node, bonus_token, st)
+               : predraw_impl<float, false>(p, parents, tokens, R, B, V, sL, ws, uniforms, n_draws, node_draw, exit_node, bonus_token, st);
 }
 
 hipError_t launch_residual_cdf(const void *logits, int dtype, bool vec, const int32_t *parents,

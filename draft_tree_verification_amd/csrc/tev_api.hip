@@ -91,6 +91,26 @@ tev_status tev_sample(const void *logits, int dtype, const int32_t *parents,
                                     (hipStream_t)stream));
 }
 
+tev_status tev_predraw(const void *logits, int dtype, const int32_t *parents,
+                       const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                       const void *workspace, size_t workspace_bytes, const float *uniforms,
+                       int n_draws, int32_t *node_draw, int32_t *exit_node,
+                       int32_t *bonus_token, void *stream) {
+    if (!logits || !parents || !tokens || !workspace || !uniforms || !node_draw || !exit_node ||
+        !bonus_token)
+        return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    tev_status s = check_exit_shape(R, B, V);
+    if (s != TEV_OK) return s;
+    if (R > 65535 || n_draws < 1 || n_draws > 65535) return TEV_ERR_SHAPE;
+    if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
+    if (workspace_bytes < exit_ws_layout(R, B, V).total) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_predraw(logits, dtype, vec_ok(logits, dtype, V), parents, tokens, R, B,
+                                     V, log2e_scale(inv_temperature), (const char *)workspace,
+                                     uniforms, n_draws, node_draw, exit_node, bonus_token,
+                                     (hipStream_t)stream));
+}
+
 size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {
     if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0) return 0;
     if (D != 64 && D != 128) return 0;

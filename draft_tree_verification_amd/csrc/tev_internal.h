@@ -122,6 +122,10 @@ hipError_t launch_sample(const void *logits, int dtype, bool vec, const int32_t 
                          const int32_t *tokens, int R, int B, int V, float sL, const char *ws,
                          const float *uniforms, int n_draws, int32_t *exit_node,
                          int32_t *bonus_token, hipStream_t st);
+hipError_t launch_predraw(const void *logits, int dtype, bool vec, const int32_t *parents,
+                          const int32_t *tokens, int R, int B, int V, float sL, const char *ws,
+                          const float *uniforms, int n_draws, int32_t *node_draw,
+                          int32_t *exit_node, int32_t *bonus_token, hipStream_t st);
 hipError_t launch_residual_cdf(const void *logits, int dtype, bool vec, const int32_t *parents,
                                const int32_t *tokens, int R, int B, int V, float sL,
                                const char *ws, int r, int node, double *cdf, hipStream_t st);

@@ -31,7 +31,7 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
-            "tev_verify_round_timed"]
+            "tev_verify_round_timed", "tev_predraw"]
 
 
 class TevError(RuntimeError):
@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.tev_exit_law_workspace_bytes.restype = sz
         L.tev_exit_law.argtypes = [vp, i, vp, vp, i, i, i, f, vp, vp, vp, vp, vp, sz, vp]
         L.tev_sample.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp]
+        L.tev_predraw.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp, vp]
         L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.tev_tree_attn_workspace_bytes.restype = sz
         L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
@@ -69,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
-        for fn in ("tev_exit_law", "tev_sample", "tev_tree_attn", "tev_validate_tree_host",
+        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -168,6 +169,29 @@ def tev_sample(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor
                           float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
                           n, _p(out[0]), _p(out[1]), _stream())
     _check("tev_sample", st)
+    return out
+
+
+def tev_predraw(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                workspace: torch.Tensor, uniforms: torch.Tensor, inv_temperature: float = 1.0,
+                out: tuple[torch.Tensor, torch.Tensor, torch.Tensor] | None = None):
+    """Predraw-and-follow verification; uniforms float32 [R][n][B].
+    Returns (node_draw [R][n][B], exit_node [R][n], bonus_token [R][n]), int32."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    _need_cuda(logits, parents, tokens, workspace, uniforms)
+    R, B, V = logits.shape
+    n = uniforms.shape[-2]
+    if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * B:
+        raise ValueError("uniforms must be float32 [R][n][B]")
+    if out is None:
+        out = (torch.empty((R, n, B), dtype=torch.int32, device=logits.device),
+               torch.empty((R, n), dtype=torch.int32, device=logits.device),
+               torch.empty((R, n), dtype=torch.int32, device=logits.device))
+    st = lib().tev_predraw(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
+                           float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
+                           n, _p(out[0]), _p(out[1]), _p(out[2]), _stream())
+    _check("tev_predraw", st)
     return out
 
 

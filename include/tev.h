@@ -118,6 +118,30 @@ tev_status tev_sample(const void *logits, int dtype, const int32_t *parents,
                       int32_t *exit_node, int32_t *bonus_token, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Predraw-and-follow verification ([EXIT] App. A.4.1), the verifier TEV is
+ * measured against: same inputs, same law of (exit node, bonus token).
+ *
+ * Every node v draws R_v from its full target row p_v (children included):
+ * the smallest token a with u_v * T_v < R_{v,a}, R_{v,a} the running sum of
+ * p_v in token-id order and T_v its total.  The walk starts at the root; at
+ * node v it moves to the child whose incoming token equals R_v and stops when
+ * none does: exit node v, bonus token R_v.
+ *
+ * uniforms    float [R][n_draws][B]: u_v in [0, 1) for every node of every draw.
+ * node_draw   int32 [R][n_draws][B] output: R_v of every node.
+ * exit_node, bonus_token  int32 [R][n_draws] outputs.
+ * `workspace` must be the one filled by tev_exit_law for the same logits,
+ * tree, sizes and inv_temperature, earlier on the same stream (the draws use
+ * its per-chunk row sums); it is not modified.  R <= 65535, n_draws <= 65535.
+ * A request flagged by tev_exit_law gets -1 in every output.
+ * ------------------------------------------------------------------------ */
+tev_status tev_predraw(const void *logits, int dtype, const int32_t *parents,
+                       const int32_t *tokens, int R, int B, int V, float inv_temperature,
+                       const void *workspace, size_t workspace_bytes, const float *uniforms,
+                       int n_draws, int32_t *node_draw, int32_t *exit_node,
+                       int32_t *bonus_token, void *stream);
+
+/* ------------------------------------------------------------------------
  * One layer of ancestor-masked tree attention ([CAST] App. B Lemma 1 and
  * App. C "Packed verification": every packed node attends to all P cached
  * prefix entries and to the entries of its own root path, itself included).
