@@ -198,6 +198,30 @@ def predraw(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndar
     return PredrawDraws(nd, en, bt, band.astype(bool))
 
 
+def commit_kv(k: np.ndarray, v: np.ndarray, parents: np.ndarray, exit_node: np.ndarray, P: int):
+    """Cache commit after verification (2610.00321 App. C "Packed
+    verification": the accepted root path keeps its packed entries, compacted
+    after the prefix).  k, v [L][R][Hkv][P+B][D] (not modified);
+    exit_node [R].  For the root path 0 = a_0, ..., a_A = V of each request,
+    row P + d of the result is row P + a_d of the input (d = 0..A); every other
+    row is copied unchanged.  Returns (k', v', new_len [R] = P + A + 1)."""
+    k2, v2 = np.array(k, copy=True), np.array(v, copy=True)
+    R = k.shape[1]
+    B = k.shape[3] - P
+    par = np.asarray(parents).reshape(R, B)
+    new_len = np.empty(R, np.int32)
+    for r in range(R):
+        path = [int(exit_node[r])]
+        while path[-1] != 0:
+            path.append(int(par[r, path[-1]]))
+        path.reverse()
+        for d, a in enumerate(path):
+            k2[:, r, :, P + d] = k[:, r, :, P + a]
+            v2[:, r, :, P + d] = v[:, r, :, P + a]
+        new_len[r] = P + len(path)
+    return k2, v2, new_len
+
+
 def residual_cdf(logits_req: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
                  node: int, inv_temperature: float = 1.0) -> np.ndarray:
     """Normalised residual CDF of one node's row in token order (Eq. 7)."""
