@@ -258,6 +258,16 @@ def main():
     def call_sample(s):
         tev.tev_sample(s["lg"], s["par"], s["tok"], ws_e, s["uni"], wl.inv_temperature, out=draws)
 
+    # Predraw-and-follow (the pages' baseline verifier): one uniform per node
+    pd_uni = torch.from_numpy((np.random.default_rng(7).integers(0, 1 << 24, size=(R, 1, B))
+                               * 2.0 ** -24).astype(np.float32)).cuda()
+    pd_out = (torch.empty((R, 1, B), dtype=torch.int32, device="cuda"),
+              torch.empty((R, 1), dtype=torch.int32, device="cuda"),
+              torch.empty((R, 1), dtype=torch.int32, device="cuda"))
+
+    def call_predraw(s):
+        tev.tev_predraw(s["lg"], s["par"], s["tok"], ws_e, pd_uni, wl.inv_temperature, out=pd_out)
+
     def step_separate(s):
         call_attn(s)
         call_exit(s)
@@ -370,23 +380,33 @@ def main():
                 for j, nm in enumerate(names)}
     log("[bench] round launches (us): " + ", ".join(f"{k} {v:.2f}" for k, v in phase_us.items()))
 
-    # per-call durations of the three separate calls (graph replays, same ring)
+    # per-call durations of the separate calls: graphs of G consecutive calls
+    # on distinct ring slots, as the round itself is timed
     per_call = {}
-    for name, fn in (("tev_tree_attn", call_attn), ("tev_exit_law", call_exit), ("tev_sample", call_sample)):
-        gs = capture(fn)
+    call_exit(slots[0])   # a filled exit-law workspace for the draw calls
+    for name, fn in (("tev_tree_attn", call_attn), ("tev_exit_law", call_exit), ("tev_sample", call_sample),
+                     ("tev_predraw", call_predraw)):
+        gs = []
         with torch.cuda.stream(stream):
-            for i in range(10):
-                gs[i % ring].replay()
+            for j in range(n_multi):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for t in range(G):
+                        fn(slots[j * G + t])
+                gs.append(g)
+            for i in range(2):
+                gs[i % n_multi].replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.call_iters // G)
         with torch.cuda.stream(stream):
             a.record(stream)
-            for i in range(args.call_iters):
-                gs[i % ring].replay()
+            for i in range(reps):
+                gs[i % n_multi].replay()
             b.record(stream)
         torch.cuda.synchronize()
-        per_call[name] = a.elapsed_time(b) / args.call_iters * 1e3   # us
+        per_call[name] = a.elapsed_time(b) / (reps * G) * 1e3   # us
         del gs
     log(f"[bench] per call (us): " + ", ".join(f"{k} {v:.2f}" for k, v in per_call.items()))
 
@@ -416,6 +436,9 @@ def main():
         "k_round_tail": {"us": round(phase_us["k_round_tail"], 3),
                          "note": "draw workgroups + the attention split combine"},
         "separate_calls_us": {k: round(v, 3) for k, v in per_call.items()},
+        "verifier_decision_us": {"tev_sample (exit node + bonus)": round(per_call["tev_sample"], 3),
+                                 "tev_predraw (B node draws + walk)": round(per_call["tev_predraw"], 3),
+                                 "note": "both after the same tev_exit_law; one draw per request"},
     }
     dominant = max(("k_vocab", "k_round_attn"), key=phase_us.get)
     roof = dict(kernels[dominant])

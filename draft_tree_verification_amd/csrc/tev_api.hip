@@ -111,6 +111,19 @@ tev_status tev_predraw(const void *logits, int dtype, const int32_t *parents,
                                      (hipStream_t)stream));
 }
 
+tev_status tev_commit_kv(void *k, void *v, int dtype, const int32_t *parents,
+                         const int32_t *exit_node, int R, int B, int L, int Hkv, int D, int P,
+                         int32_t *new_len, void *stream) {
+    if (!k || !v || !parents || !exit_node || !new_len) return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    if (R < 1 || B < 1 || B > TEV_MAX_NODES || L < 1 || Hkv < 1 || P < 0) return TEV_ERR_SHAPE;
+    if ((long long)L * R * Hkv > 0x7fffffffLL) return TEV_ERR_SHAPE;
+    if (D != 64 && D != 128) return TEV_ERR_UNSUPPORTED;
+    if ((uintptr_t)k % 16 || (uintptr_t)v % 16) return TEV_ERR_UNSUPPORTED;
+    return hip_status(launch_commit_kv(k, v, dtype, parents, exit_node, R, B, L, Hkv, D, P, new_len,
+                                       (hipStream_t)stream));
+}
+
 size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {
     if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0) return 0;
     if (D != 64 && D != 128) return 0;

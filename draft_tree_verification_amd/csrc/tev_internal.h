@@ -126,6 +126,9 @@ hipError_t launch_predraw(const void *logits, int dtype, bool vec, const int32_t
                           const int32_t *tokens, int R, int B, int V, float sL, const char *ws,
                           const float *uniforms, int n_draws, int32_t *node_draw,
                           int32_t *exit_node, int32_t *bonus_token, hipStream_t st);
+hipError_t launch_commit_kv(void *k, void *v, int dtype, const int32_t *parents,
+                            const int32_t *exit_node, int R, int B, int L, int Hkv, int D, int P,
+                            int32_t *new_len, hipStream_t st);
 hipError_t launch_residual_cdf(const void *logits, int dtype, bool vec, const int32_t *parents,
                                const int32_t *tokens, int R, int B, int V, float sL,
                                const char *ws, int r, int node, double *cdf, hipStream_t st);

@@ -31,7 +31,7 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
-            "tev_verify_round_timed", "tev_predraw"]
+            "tev_verify_round_timed", "tev_predraw", "tev_commit_kv"]
 
 
 class TevError(RuntimeError):
@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.tev_exit_law.argtypes = [vp, i, vp, vp, i, i, i, f, vp, vp, vp, vp, vp, sz, vp]
         L.tev_sample.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp]
         L.tev_predraw.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp, vp]
+        L.tev_commit_kv.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, i, vp, vp]
         L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.tev_tree_attn_workspace_bytes.restype = sz
         L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
-        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_tree_attn", "tev_validate_tree_host",
+        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -192,6 +193,25 @@ def tev_predraw(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tenso
                            float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
                            n, _p(out[0]), _p(out[1]), _p(out[2]), _stream())
     _check("tev_predraw", st)
+    return out
+
+
+def tev_commit_kv(k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor, exit_node: torch.Tensor,
+                  P: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """In-place cache commit: k, v [L][R][Hkv][P+B][D] (or [R][Hkv][P+B][D] for
+    one layer); exit_node int32 [R].  Returns new_len int32 [R]."""
+    _need_cuda(k, v, parents, exit_node)
+    if k.dim() == 4:
+        k, v = k.unsqueeze(0), v.unsqueeze(0)
+    L, R, Hkv, nkv, D = k.shape
+    B = nkv - P
+    if v.shape != k.shape or v.dtype != k.dtype or parents.numel() != R * B or exit_node.numel() != R:
+        raise ValueError("k/v [L][R][Hkv][P+B][D], parents [R][B], exit_node [R]")
+    if out is None:
+        out = torch.empty((R,), dtype=torch.int32, device=k.device)
+    st = lib().tev_commit_kv(_p(k), _p(v), _dtype_code(k), _p(parents), _p(exit_node), R, B, L, Hkv,
+                             D, int(P), _p(out), _stream())
+    _check("tev_commit_kv", st)
     return out
 
 

@@ -208,6 +208,27 @@ tev_status tev_verify_round_timed(const void *q, const void *k, const void *v,
                                   size_t workspace_bytes, void *stream, void *const *events);
 
 /* ------------------------------------------------------------------------
+ * KV-cache commit after verification ([CAST] App. C "Packed verification":
+ * only the accepted root path keeps its packed cache entries; [EXIT] the
+ * verifier stage's cache commit).
+ *
+ * k, v      [L][R][Hkv][P + B][D] (L layers), dtype TEV_BF16 or TEV_F32,
+ *           16-byte aligned; modified IN PLACE.
+ * exit_node int32 [R]: the accepted node V of each request (e.g. the first
+ *           column of tev_sample's output); its root path is
+ *           0 = a_0, a_1, ..., a_A = V with A = depth(V).
+ * For every layer, request and kv head, cache row P + a_d moves to row P + d
+ * (d = 0..A); rows 0..P-1 and rows past P + A keep their contents.
+ * new_len   int32 [R] output: P + A + 1, the committed cache length, or -1
+ *           when V is out of range or the parents on its root path violate
+ *           the tree contract (nothing of that request is moved).
+ * D must be 64 or 128.  Calls on the same cache must not overlap.
+ * ------------------------------------------------------------------------ */
+tev_status tev_commit_kv(void *k, void *v, int dtype, const int32_t *parents,
+                         const int32_t *exit_node, int R, int B, int L, int Hkv, int D, int P,
+                         int32_t *new_len, void *stream);
+
+/* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
 
