@@ -76,9 +76,15 @@ class HipEvent:
         return ms.value * 1e3
 
 
+# The sources the round's three kernels (vocabulary pass, attention, tail) are
+# compiled from; counters stored for them stay valid while these are unchanged.
+ROUND_SOURCES = ("exit_law.hip", "exit_law_dev.h", "round.hip", "tev_internal.h",
+                 "tree_attn.hip", "tree_attn_dev.h", "wave_ops.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in ROUND_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
