@@ -12,7 +12,8 @@ arrays.  Sources:
 * "Where Draft Trees Lose Target Mass: Exit-Guided Speculative Decoding"
   (arXiv 2610.11750): Sec. 3 Eq. 1-2 (p_v, reach P), Sec. 3.1 Eq. 4 (A(v),
   rho, w), Lemma 1 Eq. 5, Sec. 3.2 Eq. 6 (coverage), Eq. 7 (residual law),
-  App. B Algorithm 1 (TEV's two draws).
+  App. B Algorithm 1 (TEV's two draws), Sec. 5 Eq. 14 (the exit-guided
+  draft-tree loss, ``exit_loss``).
 * "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
   (arXiv 2610.00321): App. B Lemma 1 and App. C "Packed verification"
   (ancestor-only attention mask).
@@ -220,6 +221,83 @@ def commit_kv(k: np.ndarray, v: np.ndarray, parents: np.ndarray, exit_node: np.n
             v2[:, r, :, P + d] = v[:, r, :, P + a]
         new_len[r] = P + len(path)
     return k2, v2, new_len
+
+
+@dataclass
+class ExitLoss:
+    loss: float              # L_exit
+    numerator: float         # sum of w(v) * (-log q) over every non-root node
+    row_lse: np.ndarray      # [R][H] logsumexp of every draft-logit row
+    row_weight: np.ndarray   # [R][H] summed weight of the nodes scored by the row
+    grad: np.ndarray         # [R][H][V] d L_exit / d draft_logits
+
+
+def _logsumexp64(z: np.ndarray) -> float:
+    """log sum_a exp(z_a) in fp64, shifted by the maximum; -inf for an all -inf row."""
+    m = float(np.max(z))
+    if m == -np.inf:
+        return -np.inf
+    return m + float(np.log(np.sum(np.exp(z - m))))
+
+
+def exit_loss(draft_logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
+              weights: np.ndarray) -> ExitLoss:
+    """Exit-guided draft-tree loss ("Where Draft Trees Lose Target Mass",
+    Sec. 5 Eq. 14) and its gradient in the draft logits.
+
+    draft_logits [R][H][V]: row (r, d - 1) holds the drafter's position-wise
+    logits for future draft position d = 1..H of example r, shared by every
+    node of depth d (Sec. 5; App. C.2 row(v)).  weights [R][B] are the
+    detached exit weights w(v); tokens [R][B] the incoming draft tokens x_v.
+
+    Written node by node as Eq. 14 states it: each non-root node v of depth d
+    contributes w(v) * (-log q_d(x_v)), with log q_d = z - logsumexp(z) of its
+    own row (one logsumexp per node: none of App. C.2's sharing), and the sum
+    over the minibatch is divided by the number of non-root nodes,
+    sum_i (|V_i| - 1) = R (B - 1).  Readings: a node whose weight is exactly 0
+    contributes nothing (so a zero-probability token under a zero weight is
+    not 0 * inf); with no non-root node the loss and gradient are 0; a node
+    deeper than H has no draft row and is an error.
+
+    The gradient of -log q_d(x_v) in row d's logits is softmax(z) - e_{x_v};
+    grad sums w(v) times it over the row's nodes, divided by the same count.
+    row_weight[r][d-1] is the sum of w(v) over the row's nonzero-weight nodes
+    (Eq. 67's per-row factor), reported alongside."""
+    z = _as_input(draft_logits, dtype)
+    if dtype == "bf16":                                   # bf16 = upper half of a binary32
+        z = (z.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    z = z.astype(np.float64)
+    R, H, V = z.shape
+    par = np.asarray(parents, dtype=np.int64).reshape(R, -1)
+    tok = np.asarray(tokens, dtype=np.int64).reshape(R, -1)
+    w = np.asarray(weights, dtype=np.float64).reshape(R, -1)
+    B = par.shape[1]
+    n_nodes = R * (B - 1)
+    row_lse = np.array([[_logsumexp64(z[r, d]) for d in range(H)] for r in range(R)])
+    row_weight = np.zeros((R, H))
+    grad = np.zeros((R, H, V))
+    num = 0.0
+    for r in range(R):
+        if not check_tree(par[r].astype(np.int32), tok[r].astype(np.int32), V):
+            raise OracleError(f"request {r}: invalid tree")
+        depth = np.zeros(B, np.int64)
+        for v in range(1, B):
+            depth[v] = depth[par[r, v]] + 1
+            if depth[v] > H:
+                raise OracleError(f"request {r}: node {v} has depth {depth[v]} > H = {H}")
+        for v in range(1, B):
+            if w[r, v] == 0.0:
+                continue
+            row = z[r, depth[v] - 1]
+            lse = _logsumexp64(row)                       # this node's own normaliser
+            num += w[r, v] * (lse - row[tok[r, v]])       # w(v) * (-log q_d(x_v))
+            row_weight[r, depth[v] - 1] += w[r, v]
+            g = np.exp(row - lse)
+            g[tok[r, v]] -= 1.0
+            grad[r, depth[v] - 1] += w[r, v] * g
+    if n_nodes == 0:
+        return ExitLoss(0.0, 0.0, row_lse, row_weight, grad)
+    return ExitLoss(num / n_nodes, num, row_lse, row_weight, grad / n_nodes)
 
 
 def residual_cdf(logits_req: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
