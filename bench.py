@@ -416,6 +416,62 @@ def main():
         del gs
     log(f"[bench] per call (us): " + ", ".join(f"{k} {v:.2f}" for k, v in per_call.items()))
 
+    # the exit-guided draft-tree loss on the workload's own draft rows, weighted
+    # by the exit masses the exit law just produced (loss alone, then with the
+    # gradient), graphs of consecutive calls over a ring of draft-row copies
+    exit_loss = None
+    try:
+        zrows = W.draft_rows(wl.name)
+    except KeyError:
+        zrows = None
+    if zrows is not None:
+        H = zrows.shape[1]
+        z0 = to_dev(zrows)
+        zring = [z0] + [z0.clone() for _ in range(max(1, min(64, int(np.ceil(
+            args.ring_bytes / (z0.numel() * z0.element_size()))))) - 1)]
+        el_w = el_out.exit_mass.clone()
+        ws_l = torch.empty(tev.tev_exit_loss_workspace_bytes(R, B, H, V), dtype=torch.uint8, device="cuda")
+        lo = tev.ExitLossResult(torch.empty(1, dtype=torch.float32, device="cuda"),
+                                torch.empty((R, H), dtype=torch.float32, device="cuda"),
+                                torch.empty((R, H), dtype=torch.float32, device="cuda"), None, ws_l)
+        lo_g = tev.ExitLossResult(lo.loss, lo.row_lse, lo.row_weight,
+                                  torch.empty((R, H, V), dtype=torch.float32, device="cuda"), ws_l)
+        exit_loss = {"rows": R * H, "vocab": V, "copies": len(zring)}
+        esz = z0.element_size()
+        for name, o, nbytes in (("loss", lo, R * H * V * esz), ("loss_and_grad", lo_g, R * H * V * (2 * esz + 4))):
+            def fn(j, o=o):
+                tev.tev_exit_loss(zring[j % len(zring)], base["par"], base["tok"], el_w, out=o)
+            gs = []
+            with torch.cuda.stream(stream):
+                for j in range(n_multi):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        for t in range(G):
+                            fn(j * G + t)
+                    gs.append(g)
+                for i in range(2):
+                    gs[i % n_multi].replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            reps = max(1, args.call_iters // G)
+            with torch.cuda.stream(stream):
+                a.record(stream)
+                for i in range(reps):
+                    gs[i % n_multi].replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / (reps * G) * 1e3
+            del gs
+            gbs = nbytes / (us * 1e-6) / 1e9
+            exit_loss[name] = {"us": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                               "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        exit_loss["loss_value"] = float(lo.loss[0])
+        log(f"[bench] tev_exit_loss over {R * H} draft rows: loss {exit_loss['loss']['us']:.2f} us, "
+            f"loss + grad {exit_loss['loss_and_grad']['us']:.2f} us "
+            f"({exit_loss['loss_and_grad']['achieved_gbs']:.0f} GB/s)")
+        del zring
+
     work = algorithmic_work(wl)
     attn_hbm_bound = work["attn_bytes"] / HBM_PEAK_GBS > work["attn_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e3
 
@@ -445,6 +501,7 @@ def main():
         "verifier_decision_us": {"tev_sample (exit node + bonus)": round(per_call["tev_sample"], 3),
                                  "tev_predraw (B node draws + walk)": round(per_call["tev_predraw"], 3),
                                  "note": "both after the same tev_exit_law; one draw per request"},
+        "tev_exit_loss": exit_loss,
     }
     dominant = max(("k_vocab", "k_round_attn"), key=phase_us.get)
     roof = dict(kernels[dominant])

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "exit_loss.h"
 #include "tev_internal.h"
 
 using namespace tev;
@@ -124,6 +125,30 @@ tev_status tev_commit_kv(void *k, void *v, int dtype, const int32_t *parents,
                                        (hipStream_t)stream));
 }
 
+size_t tev_exit_loss_workspace_bytes(int R, int B, int H, int V) {
+    if (R < 1 || B < 1 || B > TEV_MAX_NODES || H < 1 || H > LOSS_MAX_H || V < 1 || V > kMaxV)
+        return 0;
+    if ((long long)R * H > 65535) return 0;
+    return loss_ws_layout(R, B, H, V).total;
+}
+
+tev_status tev_exit_loss(const void *draft_logits, int dtype, const int32_t *parents,
+                         const int32_t *tokens, const float *weights, int R, int B, int H, int V,
+                         float *loss, float *row_lse, float *row_weight, float *grad,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (!draft_logits || !parents || !tokens || !weights || !loss || !row_lse || !row_weight ||
+        !workspace)
+        return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    const size_t need = tev_exit_loss_workspace_bytes(R, B, H, V);
+    if (need == 0) return TEV_ERR_SHAPE;
+    if (workspace_bytes < need) return TEV_ERR_WORKSPACE;
+    const bool vec = vec_ok(draft_logits, dtype, V) && ((uintptr_t)grad % 16 == 0);
+    return hip_status(launch_exit_loss(draft_logits, dtype, vec, parents, tokens, weights, R, B, H, V,
+                                       loss, row_lse, row_weight, grad, (char *)workspace,
+                                       (hipStream_t)stream));
+}
+
 size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {
     if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0) return 0;
     if (D != 64 && D != 128) return 0;
@@ -218,8 +243,8 @@ tev_status tev_read_device_status(const void *workspace, int kind, int R, int B,
                                   uint32_t *flags_host, void *stream) {
     if (!workspace || !flags_host) return TEV_ERR_NULL;
     if (R < 1) return TEV_ERR_SHAPE;
-    if (kind != 0 && kind != 1 && kind != 2) return TEV_ERR_SHAPE;
-    // Both layouts place the status words first.
+    if (kind < 0 || kind > 3) return TEV_ERR_SHAPE;
+    // Every layout places the status words first.
     hipError_t e = hipMemcpyAsync(flags_host, workspace, sizeof(uint32_t) * (size_t)R,
                                   hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);

@@ -31,7 +31,8 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_tree_attn_workspace_bytes", "tev_tree_attn", "tev_validate_tree_host",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
-            "tev_verify_round_timed", "tev_predraw", "tev_commit_kv"]
+            "tev_verify_round_timed", "tev_predraw", "tev_commit_kv",
+            "tev_exit_loss_workspace_bytes", "tev_exit_loss"]
 
 
 class TevError(RuntimeError):
@@ -57,6 +58,9 @@ def lib() -> ctypes.CDLL:
         L.tev_sample.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp]
         L.tev_predraw.argtypes = [vp, i, vp, vp, i, i, i, f, vp, sz, vp, i, vp, vp, vp, vp]
         L.tev_commit_kv.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, i, vp, vp]
+        L.tev_exit_loss_workspace_bytes.argtypes = [i, i, i, i]
+        L.tev_exit_loss_workspace_bytes.restype = sz
+        L.tev_exit_loss.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
         L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.tev_tree_attn_workspace_bytes.restype = sz
         L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
@@ -71,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
-        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_tree_attn", "tev_validate_tree_host",
+        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_exit_loss",
+                   "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -212,6 +217,51 @@ def tev_commit_kv(k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor, exit_
     st = lib().tev_commit_kv(_p(k), _p(v), _dtype_code(k), _p(parents), _p(exit_node), R, B, L, Hkv,
                              D, int(P), _p(out), _stream())
     _check("tev_commit_kv", st)
+    return out
+
+
+# ---------------------------------------------------------------- exit-guided loss
+@dataclass
+class ExitLossResult:
+    loss: torch.Tensor        # float32 [1]
+    row_lse: torch.Tensor     # float32 [R][H]
+    row_weight: torch.Tensor  # float32 [R][H]
+    grad: torch.Tensor | None  # float32 [R][H][V] or None
+    workspace: torch.Tensor   # uint8; its first R words are the flag words
+
+
+def tev_exit_loss_workspace_bytes(R: int, B: int, H: int, V: int) -> int:
+    return int(lib().tev_exit_loss_workspace_bytes(R, B, H, V))
+
+
+def tev_exit_loss(draft_logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                  weights: torch.Tensor, with_grad: bool = True,
+                  workspace: torch.Tensor | None = None,
+                  out: ExitLossResult | None = None) -> ExitLossResult:
+    """Exit-guided draft-tree loss: draft_logits [R][H][V] (bf16 or f32),
+    parents/tokens int32 [R][B], weights float32 [R][B], all on the GPU."""
+    _need_cuda(draft_logits, parents, tokens, weights)
+    R, H, V = draft_logits.shape
+    B = parents.shape[-1]
+    if parents.numel() != R * B or tokens.numel() != R * B or weights.numel() != R * B:
+        raise ValueError("parents, tokens and weights must be [R][B]")
+    if weights.dtype != torch.float32:
+        raise TypeError("weights must be float32")
+    dev = draft_logits.device
+    if out is None:
+        if workspace is None:
+            workspace = torch.empty(max(tev_exit_loss_workspace_bytes(R, B, H, V), 1),
+                                    dtype=torch.uint8, device=dev)
+        out = ExitLossResult(torch.empty(1, dtype=torch.float32, device=dev),
+                             torch.empty((R, H), dtype=torch.float32, device=dev),
+                             torch.empty((R, H), dtype=torch.float32, device=dev),
+                             torch.empty((R, H, V), dtype=torch.float32, device=dev)
+                             if with_grad else None, workspace)
+    st = lib().tev_exit_loss(_p(draft_logits), _dtype_code(draft_logits), _p(parents), _p(tokens),
+                             _p(weights), R, B, H, V, _p(out.loss), _p(out.row_lse),
+                             _p(out.row_weight), _p(out.grad), _p(out.workspace),
+                             out.workspace.numel(), _stream())
+    _check("tev_exit_loss", st)
     return out
 
 

@@ -292,8 +292,12 @@ def _request_tiny(cfg, r):
     return parents, tokens, logits.astype(np.float32)
 
 
+def _qwen_ell(cfg, r, L=16, V=V_QWEN):
+    return _peaked_draft(_rng(cfg, r, S_DRAFT), L + 1, V)
+
+
 def _request_qwen_peaked(cfg, r, B, L=16, V=V_QWEN):
-    ell = _peaked_draft(_rng(cfg, r, S_DRAFT), L + 1, V)
+    ell = _qwen_ell(cfg, r, L, V)
     parents, tokens = best_first_tree(_softmax64(ell[:L]), B)
     tokens[0] = _rng(cfg, r, S_ROOT).integers(0, V)
     d = depths_of(parents)
@@ -302,11 +306,16 @@ def _request_qwen_peaked(cfg, r, B, L=16, V=V_QWEN):
     return parents, tokens, f32_to_bf16_bits(logits)
 
 
-def _request_wide_zipf(cfg, r, B=128, L=16, V=V_QWEN):
+def _wide_ell(cfg, r, L=16, V=V_QWEN):
     rng = _rng(cfg, r, S_DRAFT)
     ell = rng.standard_normal(size=(L + 1, V)) * 4.0
     top = np.argpartition(-ell, 8, axis=1)[:, :8]
     np.put_along_axis(ell, top, 20.0 + rng.standard_normal(size=top.shape) * 0.5, axis=1)
+    return ell
+
+
+def _request_wide_zipf(cfg, r, B=128, L=16, V=V_QWEN):
+    ell = _wide_ell(cfg, r, L, V)
     q = _softmax64(ell)
     parents, tokens = best_first_tree(q[:L], B)
     tokens[0] = _rng(cfg, r, S_ROOT).integers(0, V)
@@ -429,6 +438,28 @@ def make_config(name: str, n_uniform: int = 4096, with_attention: bool = True,
         w.q, w.k, w.v = make_attention(cfg, R, B, Hq, Hkv, D, P, dtype)
     w.meta["description"] = DESCRIPTIONS[name]
     return w
+
+
+def draft_rows(name: str, requests: int | None = None) -> np.ndarray:
+    """The position-wise draft logits a named workload's trees were built from:
+    [R][L][V], row j scoring the nodes of depth j + 1 (the drafter's rows for
+    the exit-guided loss).  f32 for "tiny", bf16 bits otherwise.  The mixture
+    workload has K draft modes rather than one row per position: KeyError."""
+    cfg, R, B, V, dtype, *_ = CONFIGS[name]
+    if requests is not None:
+        R = min(R, int(requests))
+    rows = []
+    for r in range(R):
+        if name == "tiny":
+            rows.append(_rng(cfg, r, S_DRAFT).standard_normal(size=(4, V)) * 3.0)
+        elif name in ("qwen3_4b", "batched"):
+            rows.append(_qwen_ell(cfg, r)[:16])
+        elif name == "qwen3_8b_wide":
+            rows.append(_wide_ell(cfg, r)[:16])
+        else:
+            raise KeyError(f"{name} has no single position-wise drafter")
+    z = np.stack(rows).astype(np.float32)
+    return z if dtype == "f32" else f32_to_bf16_bits(z)
 
 
 def make_custom(name: str, *, R: int = 1, B: int = 16, V: int = 1000, dtype: str = "f32",

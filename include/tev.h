@@ -33,7 +33,8 @@
  * Sources (titles of the pages the operations are defined on):
  *  [EXIT] "Where Draft Trees Lose Target Mass: Exit-Guided Speculative
  *         Decoding" (arXiv 2610.11750): Sec. 3 Eq. 1-2, Sec. 3.1 Eq. 4,
- *         Lemma 1 Eq. 5, Sec. 3.2 Eq. 6-7, App. B Algorithm 1.
+ *         Lemma 1 Eq. 5, Sec. 3.2 Eq. 6-7, App. B Algorithm 1, Sec. 5
+ *         Eq. 14 and App. C.2 Eq. 66-67.
  *  [CAST] "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
  *         (arXiv 2610.00321): App. B Lemma 1, App. C "Packed verification",
  *         App. F varlen tree-attention verifier.
@@ -229,6 +230,45 @@ tev_status tev_commit_kv(void *k, void *v, int dtype, const int32_t *parents,
                          int32_t *new_len, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Exit-guided draft-tree loss ([EXIT] Sec. 5 Eq. 14, evaluated per App. C.2
+ * Eq. 66-67) and its gradient in the draft logits.
+ *
+ * draft_logits [R][H][V], TEV_F32 or TEV_BF16: the drafter's position-wise
+ *           logits.  Row (r, d - 1) is future draft position d = 1..H of
+ *           example r and scores every node of depth d (depth = number of
+ *           edges from the root); nodes at one depth share the row.
+ * parents, tokens [R][B]: the realised trees (library tree contract; sibling
+ *           tokens need not be distinct here).  Every node's depth must be
+ *           <= H.
+ * weights   float [R][B]: the detached node weights w(v), e.g. the
+ *           exit_mass output of tev_exit_law.  weights[r][0] is not read.
+ *
+ *   loss  = sum_r sum_{v >= 1, w(v) != 0} w(v) (lse_{r,d(v)} - z_{r,d(v),x_v})
+ *           / (R (B - 1))                       (0 when B = 1)
+ *   lse_m = log sum_a exp(z_{m,a})             natural log, one per row
+ * A node with weight exactly 0 contributes nothing.
+ *
+ * loss        float [1] output.
+ * row_lse     float [R][H] output: lse_m of every row.
+ * row_weight  float [R][H] output: summed weight of the row's nodes.
+ * grad        float [R][H][V] output, or NULL for the loss alone:
+ *             d loss / d z_{m,a} = (row_weight_m softmax(z_m)_a
+ *                                   - sum_{v in m, x_v = a} w(v)) / (R (B - 1)).
+ * workspace   tev_exit_loss_workspace_bytes(R, B, H, V) bytes, any contents;
+ *             its first R words are the per-example flag words
+ *             (tev_read_device_status kind 3).
+ * A flagged example (invalid tree, a node deeper than H, a NaN or +inf logit
+ * or an all -inf row in any of its rows) makes its row outputs, its gradient
+ * rows and the loss NaN.  Limits: 1 <= H <= 1024, R * H <= 65535.
+ * ------------------------------------------------------------------------ */
+size_t tev_exit_loss_workspace_bytes(int R, int B, int H, int V);
+
+tev_status tev_exit_loss(const void *draft_logits, int dtype, const int32_t *parents,
+                         const int32_t *tokens, const float *weights, int R, int B, int H, int V,
+                         float *loss, float *row_lse, float *row_weight, float *grad,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
 
@@ -238,10 +278,11 @@ tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *to
                                   int B, int V);
 
 /* Copies the R per-request flag words (TEV_FLAG_*) of an exit-law,
- * tree-attention or round workspace into flags_host [R].  `kind` is 0 for an
- * exit-law workspace (sizes R, B, V), 1 for a tree-attention workspace (only R
- * is used) and 2 for a tev_verify_round workspace (sizes R, B, V; the two
- * parts' flags are OR-ed).  Synchronous: waits for `stream`. */
+ * tree-attention, round or exit-loss workspace into flags_host [R].  `kind`
+ * is 0 for an exit-law workspace (sizes R, B, V), 1 for a tree-attention
+ * workspace (only R is used), 2 for a tev_verify_round workspace (sizes R, B,
+ * V; the two parts' flags are OR-ed) and 3 for a tev_exit_loss workspace
+ * (only R is used).  Synchronous: waits for `stream`. */
 tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
                                   uint32_t *flags_host, void *stream);
 
