@@ -416,6 +416,46 @@ def main():
         del gs
     log(f"[bench] per call (us): " + ", ".join(f"{k} {v:.2f}" for k, v in per_call.items()))
 
+    # cache commit of the drawn exit node's root path over a 36-layer cache of
+    # the workload's kv layout (the depth of a Qwen3-4B target); in place, so
+    # repeated commits keep permuting rows inside the tree region
+    # (the prefix rows are never touched: past 4 GB of cache the prefix is left
+    # out, P = 0, and the same rows move)
+    n_layers = 36
+    esz_kv = base["k"].element_size()
+    P_c = wl.P if 2 * n_layers * R * wl.Hkv * (wl.P + B) * wl.D * esz_kv <= (4 << 30) else 0
+    kc = torch.zeros((n_layers, R, wl.Hkv, P_c + B, wl.D), dtype=base["k"].dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    exit_nodes = draws[0][:, 0].contiguous()
+    new_len = torch.empty((R,), dtype=torch.int32, device="cuda")
+
+    def call_commit(s):
+        tev.tev_commit_kv(kc, vc, s["par"], exit_nodes, P_c, out=new_len)
+
+    gs = []
+    with torch.cuda.stream(stream):
+        for j in range(n_multi):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(G):
+                    call_commit(slots[j * G + t])
+            gs.append(g)
+        for i in range(2):
+            gs[i % n_multi].replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    reps = max(1, args.call_iters // G)
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for i in range(reps):
+            gs[i % n_multi].replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call["tev_commit_kv"] = a.elapsed_time(b) / (reps * G) * 1e3
+    del gs, kc, vc
+    log(f"[bench] tev_commit_kv ({n_layers} layers, prefix {P_c}): {per_call['tev_commit_kv']:.2f} us")
+
     # the exit-guided draft-tree loss on the workload's own draft rows, weighted
     # by the exit masses the exit law just produced (loss alone, then with the
     # gradient), graphs of consecutive calls over a ring of draft-row copies
@@ -500,6 +540,11 @@ def main():
         "separate_calls_us": {k: round(v, 3) for k, v in per_call.items()},
         "verifier_decision_us": {"tev_sample (exit node + bonus)": round(per_call["tev_sample"], 3),
                                  "tev_predraw (B node draws + walk)": round(per_call["tev_predraw"], 3),
+                                 "tev_commit_kv (36 layers)": round(per_call["tev_commit_kv"], 3),
+                                 "tev stage (sample + commit)": round(per_call["tev_sample"]
+                                                                      + per_call["tev_commit_kv"], 3),
+                                 "predraw stage (predraw + commit)": round(per_call["tev_predraw"]
+                                                                           + per_call["tev_commit_kv"], 3),
                                  "note": "both after the same tev_exit_law; one draw per request"},
         "tev_exit_loss": exit_loss,
     }
