@@ -14,6 +14,8 @@ arrays.  Sources:
   rho, w), Lemma 1 Eq. 5, Sec. 3.2 Eq. 6 (coverage), Eq. 7 (residual law),
   App. B Algorithm 1 (TEV's two draws), Sec. 5 Eq. 14 (the exit-guided
   draft-tree loss, ``exit_loss``).
+* "CAST" App. C "Candidate construction" and "Multi-Future Drafting" App. B
+  (the best-first tree builder, ``build_tree``).
 * "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
   (arXiv 2610.00321): App. B Lemma 1 and App. C "Packed verification"
   (ancestor-only attention mask).
@@ -26,6 +28,7 @@ reading together with the enumerated law.
 from __future__ import annotations
 
 import ctypes
+import heapq
 import os
 import subprocess
 from dataclasses import dataclass
@@ -298,6 +301,89 @@ def exit_loss(draft_logits: np.ndarray, dtype: str, parents: np.ndarray, tokens:
     if n_nodes == 0:
         return ExitLoss(0.0, 0.0, row_lse, row_weight, grad)
     return ExitLoss(num / n_nodes, num, row_lse, row_weight, grad / n_nodes)
+
+
+@dataclass
+class BuiltTree:
+    parents: np.ndarray    # [R][B] int32, node order = pop order
+    tokens: np.ndarray     # [R][B] int32, tokens[r][0] = the root token
+    scores: np.ndarray     # [R][B] float64, log of the plug-in prefix score (root 0)
+    near_tie: np.ndarray   # [R] bool: two keys the heap compared differ by <= tie_eps
+
+
+def build_tree(draft_logits: np.ndarray, dtype: str, topk: int, n_nodes: int,
+               root_tokens: np.ndarray, tie_eps: float = 1e-9) -> BuiltTree:
+    """Best-first draft tree over the retained universe ("CAST", App. C
+    "Candidate construction"; "Multi-Future Drafting", App. B, the merged heap
+    with one mode, i.e. DDTree's builder).
+
+    draft_logits [R][L][V]: row j is draft position j + 1.  q_j = softmax of
+    row j over the whole vocabulary (scores use the original q_j, not a
+    renormalised top-K).  Each position keeps its topk most likely tokens
+    (larger logit first, then smaller token id); rank r is the position in
+    that list.  The plug-in score of a prefix y_1..y_d is
+    prod_j q_j(y_j); its key is
+        s = (sum_j z_{j, y_j}) - (sum_j lse_j)        (= log of the score)
+    with the logit sum accumulated along the path in f64 (exact for bf16
+    logits) and the logsumexp sum per depth.
+
+    The heap holds candidate prefixes keyed by s; popping a prefix emits it
+    as the next node and pushes its next sibling (its last token replaced by
+    the one of the next rank) and its first child (the rank-0 token of the
+    next position, while its depth is below L).  It starts from the rank-0
+    token of position 1 and stops after n_nodes - 1 pops.  Equal keys go to
+    the shorter prefix, then to the lexicographically smaller rank sequence.
+
+    near_tie[r] reports whether two keys of request r that the build orders
+    (every emitted node and every entry left in the heap) differ by at most
+    tie_eps without being computed from identical logit sums."""
+    z = _as_input(draft_logits, dtype)
+    if dtype == "bf16":
+        z = (z.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    z = z.astype(np.float64)
+    R, L, V = z.shape
+    if not (1 <= topk <= V) or n_nodes < 1:
+        raise OracleError("bad topk / n_nodes")
+    universe = sum(topk ** d for d in range(1, L + 1))
+    if n_nodes - 1 > universe:
+        raise OracleError("the retained universe holds fewer prefixes than n_nodes - 1")
+    par = np.full((R, n_nodes), -1, np.int32)
+    tok = np.zeros((R, n_nodes), np.int32)
+    sc = np.zeros((R, n_nodes))
+    near = np.zeros(R, bool)
+    for r in range(R):
+        lse = np.array([_logsumexp64(z[r, j]) for j in range(L)])
+        C = np.concatenate([[0.0], np.cumsum(lse)])          # C[d] = sum of lse over depths 1..d
+        order = [np.lexsort((np.arange(V), -z[r, j]))[:topk] for j in range(L)]
+        ztop = [z[r, j, order[j]] for j in range(L)]
+        tok[r, 0] = int(root_tokens[r])
+        node_sz = [0.0]                                       # exact logit sums of the nodes
+        keys_seen = []                                        # (s, Sz, depth) of ordered keys
+
+        def entry(sz, depth, ranks, parent):
+            return (-(sz - C[depth]), depth, ranks, parent, sz)
+
+        heap = [entry(ztop[0][0], 1, (0,), 0)] if n_nodes > 1 else []
+        for n in range(1, n_nodes):
+            negs, depth, ranks, parent, sz = heapq.heappop(heap)
+            par[r, n] = parent
+            tok[r, n] = int(order[depth - 1][ranks[-1]])
+            sc[r, n] = -negs
+            node_sz.append(sz)
+            keys_seen.append((-negs, sz, depth))
+            rk = ranks[-1]
+            if rk + 1 < topk:                                 # next sibling
+                heapq.heappush(heap, entry(node_sz[parent] + ztop[depth - 1][rk + 1], depth,
+                                           ranks[:-1] + (rk + 1,), parent))
+            if depth < L:                                     # first child
+                heapq.heappush(heap, entry(sz + ztop[depth][0], depth + 1, ranks + (0,), n))
+        keys_seen += [(-e[0], e[4], e[1]) for e in heap]
+        keys_seen.sort()
+        for (s1, z1, d1), (s2, z2, d2) in zip(keys_seen, keys_seen[1:]):
+            if s2 - s1 <= tie_eps and not (z1 == z2 and d1 == d2):
+                near[r] = True
+                break
+    return BuiltTree(par, tok, sc, near)
 
 
 def residual_cdf(logits_req: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
