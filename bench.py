@@ -460,6 +460,7 @@ def main():
     # by the exit masses the exit law just produced (loss alone, then with the
     # gradient), graphs of consecutive calls over a ring of draft-row copies
     exit_loss = None
+    tree_build = None
     try:
         zrows = W.draft_rows(wl.name)
     except KeyError:
@@ -507,6 +508,39 @@ def main():
             exit_loss[name] = {"us": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         exit_loss["loss_value"] = float(lo.loss[0])
+        # the best-first tree builder on the same draft rows (B tokens kept per
+        # position, the budget of the workload's own trees)
+        Kb = min(B, 128)
+        tb = tev.tev_build_tree(zring[0], Kb, B, base["tok"][:, 0].contiguous())
+
+        def fn_tb(j):
+            tev.tev_build_tree(zring[j % len(zring)], Kb, B, out=tb)
+        gs = []
+        with torch.cuda.stream(stream):
+            for j in range(n_multi):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for t in range(G):
+                        fn_tb(j * G + t)
+                gs.append(g)
+            for i in range(2):
+                gs[i % n_multi].replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.call_iters // G)
+        with torch.cuda.stream(stream):
+            a.record(stream)
+            for i in range(reps):
+                gs[i % n_multi].replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        tb_us = a.elapsed_time(b) / (reps * G) * 1e3
+        del gs
+        tree_build = {"us": round(tb_us, 3), "K": Kb, "B": B, "rows": R * H, "vocab": V,
+                      "bytes": R * H * V * esz,
+                      "achieved_gbs": round(R * H * V * esz / (tb_us * 1e-6) / 1e9, 1)}
+        log(f"[bench] tev_build_tree over {R * H} draft rows (K={Kb}, B={B}): {tb_us:.2f} us")
         log(f"[bench] tev_exit_loss over {R * H} draft rows: loss {exit_loss['loss']['us']:.2f} us, "
             f"loss + grad {exit_loss['loss_and_grad']['us']:.2f} us "
             f"({exit_loss['loss_and_grad']['achieved_gbs']:.0f} GB/s)")
@@ -547,6 +581,7 @@ def main():
                                                                            + per_call["tev_commit_kv"], 3),
                                  "note": "both after the same tev_exit_law; one draw per request"},
         "tev_exit_loss": exit_loss,
+        "tev_build_tree": tree_build,
     }
     dominant = max(("k_vocab", "k_round_attn"), key=phase_us.get)
     roof = dict(kernels[dominant])

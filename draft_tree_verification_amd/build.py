@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libtev.so")
 SOURCES = ["tev_api.hip", "exit_law.hip", "tree_attn.hip", "round.hip", "commit.hip",
-           "exit_loss.hip"]
+           "exit_loss.hip", "tree_build.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

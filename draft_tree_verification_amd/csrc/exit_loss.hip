@@ -31,6 +31,7 @@
 
 #include "exit_law_dev.h"
 #include "exit_loss.h"
+#include "slab_dev.h"
 #include "wave_ops.h"
 
 namespace tev {
@@ -51,31 +52,6 @@ LossPtrs loss_ptrs(char *ws, const LossWs &L) {
     return LossPtrs{(unsigned *)(ws + L.status), (float *)(ws + L.slab_m), (float *)(ws + L.slab_s),
                     (double *)(ws + L.lse2),     (double *)(ws + L.omega), (double *)(ws + L.num),
                     (int32_t *)(ws + L.ent_n),   (int32_t *)(ws + L.ent_tok), (float *)(ws + L.ent_w)};
-}
-
-// Slab ownership: thread t holds elements k*(256*VW) + t*VW + j, k < EPT/VW,
-// j < VW (VW = elements per 16 bytes).  Elements at or past len read a
-// clamped valid address and become -inf; loads are unconditional.
-template <typename T, bool VEC>
-__device__ __forceinline__ void load_slab(const T *p, int len, int tid, float *x) {
-    constexpr int VW = 16 / (int)sizeof(T);
-    constexpr int SPAN = LOSS_THREADS * VW;
-#pragma unroll
-    for (int k = 0; k < LOSS_EPT / VW; k++) {
-        const int idx = k * SPAN + tid * VW;
-        if (VEC) {
-            // len is a multiple of VW (16-byte rows), so len - VW is a whole vector
-            load16(p + min(idx, len - VW), &x[k * VW]);
-#pragma unroll
-            for (int j = 0; j < VW; j++) x[k * VW + j] = (idx < len) ? x[k * VW + j] : -kInf;
-        } else {
-#pragma unroll
-            for (int j = 0; j < VW; j++) {
-                const float t = to_f32<T>(p[min(idx + j, len - 1)]);
-                x[k * VW + j] = (idx + j < len) ? t : -kInf;
-            }
-        }
-    }
 }
 
 // The same ownership for the f32 gradient: VW floats per group, stored as
@@ -111,7 +87,7 @@ __global__ __launch_bounds__(LOSS_THREADS) void k_loss_slabs(const T *__restrict
     const size_t m = blockIdx.y;
     const int start = s * LOSS_SLAB, len = min(LOSS_SLAB, V - start);
     float x[LOSS_EPT];
-    load_slab<T, VEC>(z + m * (size_t)V + start, len, tid, x);
+    load_slab<T, VEC, LOSS_THREADS, LOSS_EPT>(z + m * (size_t)V + start, len, tid, x);
     float mx = x[0];
 #pragma unroll
     for (int j = 1; j < LOSS_EPT; j++) mx = fmaxf(mx, x[j]);
@@ -283,7 +259,7 @@ __global__ __launch_bounds__(LOSS_THREADS) void k_loss_grad(const T *__restrict_
         for (int j = 0; j < LOSS_EPT; j++) val[j] = f;
     } else {
         float x[LOSS_EPT];
-        load_slab<T, VEC>(z + m * (size_t)V + start, len, tid, x);
+        load_slab<T, VEC, LOSS_THREADS, LOSS_EPT>(z + m * (size_t)V + start, len, tid, x);
         const float c = (float)(om * invN);
         const float l2 = (float)W.lse2[m];
 #pragma unroll

@@ -7,6 +7,7 @@
 
 #include "exit_loss.h"
 #include "tev_internal.h"
+#include "tree_build.h"
 
 using namespace tev;
 
@@ -149,6 +150,33 @@ tev_status tev_exit_loss(const void *draft_logits, int dtype, const int32_t *par
                                        (hipStream_t)stream));
 }
 
+size_t tev_build_tree_workspace_bytes(int R, int L, int V, int K) {
+    if (R < 1 || L < 1 || L > TB_MAX_L || V < 1 || K < 1 || K > TB_MAX_K || K > V) return 0;
+    const long long ns = tb_slabs(V);
+    if (ns > TB_MAX_SLABS || ns * K > 8192 || (long long)R * L > 65535) return 0;
+    return tree_ws_layout(R, L, V, K).total;
+}
+
+tev_status tev_build_tree(const void *draft_logits, int dtype, const int32_t *root_tokens, int R,
+                          int L, int V, int K, int B, int32_t *parents, int32_t *tokens,
+                          double *scores, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!draft_logits || !parents || !tokens || !scores || !workspace) return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    const size_t need = tev_build_tree_workspace_bytes(R, L, V, K);
+    if (need == 0 || B < 1 || B > TEV_MAX_NODES) return TEV_ERR_SHAPE;
+    // the retained universe must hold B - 1 prefixes: K + K^2 + ... + K^L
+    long long universe = 0, pw = 1;
+    for (int d = 1; d <= L && universe < B; d++) {
+        pw *= K;
+        universe += pw;
+    }
+    if (universe < B - 1) return TEV_ERR_SHAPE;
+    if (workspace_bytes < need) return TEV_ERR_WORKSPACE;
+    return hip_status(launch_build_tree(draft_logits, dtype, vec_ok(draft_logits, dtype, V), root_tokens,
+                                        R, L, V, K, B, parents, tokens, scores, (char *)workspace,
+                                        (hipStream_t)stream));
+}
+
 size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {
     if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || Hq % Hkv || P < 0) return 0;
     if (D != 64 && D != 128) return 0;
@@ -243,7 +271,7 @@ tev_status tev_read_device_status(const void *workspace, int kind, int R, int B,
                                   uint32_t *flags_host, void *stream) {
     if (!workspace || !flags_host) return TEV_ERR_NULL;
     if (R < 1) return TEV_ERR_SHAPE;
-    if (kind < 0 || kind > 3) return TEV_ERR_SHAPE;
+    if (kind < 0 || kind > 4) return TEV_ERR_SHAPE;
     // Every layout places the status words first.
     hipError_t e = hipMemcpyAsync(flags_host, workspace, sizeof(uint32_t) * (size_t)R,
                                   hipMemcpyDeviceToHost, (hipStream_t)stream);

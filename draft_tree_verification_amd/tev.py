@@ -32,7 +32,8 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_read_device_status", "tev_status_str", "tev_export_exit_cdf",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
             "tev_verify_round_timed", "tev_predraw", "tev_commit_kv",
-            "tev_exit_loss_workspace_bytes", "tev_exit_loss"]
+            "tev_exit_loss_workspace_bytes", "tev_exit_loss", "tev_build_tree_workspace_bytes",
+            "tev_build_tree"]
 
 
 class TevError(RuntimeError):
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.tev_exit_loss_workspace_bytes.argtypes = [i, i, i, i]
         L.tev_exit_loss_workspace_bytes.restype = sz
         L.tev_exit_loss.argtypes = [vp, i, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, sz, vp]
+        L.tev_build_tree_workspace_bytes.argtypes = [i, i, i, i]
+        L.tev_build_tree_workspace_bytes.restype = sz
+        L.tev_build_tree.argtypes = [vp, i, vp, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
         L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.tev_tree_attn_workspace_bytes.restype = sz
         L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
@@ -75,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
-        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_exit_loss",
+        for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_exit_loss", "tev_build_tree",
                    "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
@@ -262,6 +266,42 @@ def tev_exit_loss(draft_logits: torch.Tensor, parents: torch.Tensor, tokens: tor
                              _p(out.row_weight), _p(out.grad), _p(out.workspace),
                              out.workspace.numel(), _stream())
     _check("tev_exit_loss", st)
+    return out
+
+
+# ---------------------------------------------------------------- tree builder
+@dataclass
+class BuiltTree:
+    parents: torch.Tensor    # int32 [R][B]
+    tokens: torch.Tensor     # int32 [R][B]
+    scores: torch.Tensor     # float64 [R][B]
+    workspace: torch.Tensor  # uint8; its first R words are the flag words
+
+
+def tev_build_tree_workspace_bytes(R: int, L: int, V: int, K: int) -> int:
+    return int(lib().tev_build_tree_workspace_bytes(R, L, V, K))
+
+
+def tev_build_tree(draft_logits: torch.Tensor, K: int, B: int, root_tokens: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, out: BuiltTree | None = None) -> BuiltTree:
+    """Best-first draft tree: draft_logits [R][L][V] (bf16 or f32) on the GPU,
+    K tokens kept per position, B nodes (root included)."""
+    _need_cuda(draft_logits)
+    if root_tokens is not None:
+        _need_cuda(root_tokens)
+    R, L, V = draft_logits.shape
+    dev = draft_logits.device
+    if out is None:
+        if workspace is None:
+            workspace = torch.empty(max(tev_build_tree_workspace_bytes(R, L, V, K), 1), dtype=torch.uint8,
+                                    device=dev)
+        out = BuiltTree(torch.empty((R, B), dtype=torch.int32, device=dev),
+                        torch.empty((R, B), dtype=torch.int32, device=dev),
+                        torch.empty((R, B), dtype=torch.float64, device=dev), workspace)
+    st = lib().tev_build_tree(_p(draft_logits), _dtype_code(draft_logits), _p(root_tokens), R, L, V, K, B,
+                              _p(out.parents), _p(out.tokens), _p(out.scores), _p(out.workspace),
+                              out.workspace.numel(), _stream())
+    _check("tev_build_tree", st)
     return out
 
 

@@ -36,7 +36,8 @@
  *         Lemma 1 Eq. 5, Sec. 3.2 Eq. 6-7, App. B Algorithm 1, Sec. 5
  *         Eq. 14 and App. C.2 Eq. 66-67.
  *  [CAST] "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
- *         (arXiv 2610.00321): App. B Lemma 1, App. C "Packed verification",
+ *         (arXiv 2610.00321): App. B Lemma 1, App. C "Candidate
+ *         construction" and "Packed verification", Thm. 1,
  *         App. F varlen tree-attention verifier.
  */
 #ifndef TEV_H
@@ -269,6 +270,41 @@ tev_status tev_exit_loss(const void *draft_logits, int dtype, const int32_t *par
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Best-first draft tree ([CAST] App. C "Candidate construction" and Thm. 1;
+ * "Multi-Future Drafting: Mixture Block Drafters for Tree-Verified
+ * Speculative Decoding" App. B, the merged heap with one mode = DDTree's
+ * builder).
+ *
+ * draft_logits [R][L][V], TEV_F32 or TEV_BF16: row (r, j) is the drafter's
+ *           logits for draft position j + 1 of request r; q_j = its softmax
+ *           over the whole vocabulary.
+ * root_tokens int32 [R] (device) or NULL: written to tokens[r][0] (0 if NULL).
+ * Each position keeps its K most likely tokens (larger logit first, then the
+ * smaller token id); the tree is the B - 1 prefixes of that retained universe
+ * with the largest plug-in score prod_j q_j(y_j), in pop order (best first):
+ *   key s(v) = sum_{j <= d} z_{j, y_j} - sum_{j <= d} lse_j   (d = depth of v)
+ * with the logit sum accumulated in f64 along the path (exact for bf16
+ * logits); equal keys go to the shorter prefix, then to the lexicographically
+ * smaller sequence of ranks.
+ *
+ * parents, tokens  int32 [R][B] outputs (node 0 = root, parents[r][0] = -1,
+ *           parents[r][i] < i): the library's tree contract.
+ * scores    double [R][B] output: s(v) = log of the plug-in score (root 0).
+ * workspace tev_build_tree_workspace_bytes(R, L, V, K) bytes, any contents;
+ *           its first R words are the flag words (tev_read_device_status
+ *           kind 4).  A NaN or +inf logit, or an all -inf row, flags the
+ *           request: its tokens and parents are -1 and its scores NaN.
+ * Limits: 1 <= L <= 16, 1 <= K <= min(128, V), 1 <= B <= 256, B - 1 <= the
+ * number of prefixes of the universe (K + K^2 + ... + K^L), V <= 524288 with
+ * ceil(V / 8192) * K <= 8192, R * L <= 65535.
+ * ------------------------------------------------------------------------ */
+size_t tev_build_tree_workspace_bytes(int R, int L, int V, int K);
+
+tev_status tev_build_tree(const void *draft_logits, int dtype, const int32_t *root_tokens, int R,
+                          int L, int V, int K, int B, int32_t *parents, int32_t *tokens,
+                          double *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
 
@@ -281,8 +317,9 @@ tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *to
  * tree-attention, round or exit-loss workspace into flags_host [R].  `kind`
  * is 0 for an exit-law workspace (sizes R, B, V), 1 for a tree-attention
  * workspace (only R is used), 2 for a tev_verify_round workspace (sizes R, B,
- * V; the two parts' flags are OR-ed) and 3 for a tev_exit_loss workspace
- * (only R is used).  Synchronous: waits for `stream`. */
+ * V; the two parts' flags are OR-ed), 3 for a tev_exit_loss workspace and 4
+ * for a tev_build_tree workspace (only R is used).  Synchronous: waits for
+ * `stream`. */
 tev_status tev_read_device_status(const void *workspace, int kind, int R, int B, int V,
                                   uint32_t *flags_host, void *stream);
 

@@ -85,6 +85,23 @@ def test_argument_errors_return_before_any_launch():
     assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 2, 128, 100, float("inf"), fake, fake, need_a, s) == 8
     assert L.tev_tree_attn(fake, fake, fake, 1, null, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 1
     assert L.tev_tree_attn(fake, fake, fake, 5, fake, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 3
+    # exit-guided loss
+    need_l = L.tev_exit_loss_workspace_bytes(2, 9, 4, 1000)
+    assert need_l > 0 and L.tev_exit_loss_workspace_bytes(2, 9, 1025, 1000) == 0
+    assert L.tev_exit_loss(null, 1, fake, fake, fake, 2, 9, 4, 1000, fake, fake, fake, null, fake, need_l, s) == 1
+    assert L.tev_exit_loss(fake, 2, fake, fake, fake, 2, 9, 4, 1000, fake, fake, fake, null, fake, need_l, s) == 3
+    assert L.tev_exit_loss(fake, 1, fake, fake, fake, 2, 9, 0, 1000, fake, fake, fake, null, fake, need_l, s) == 2
+    assert L.tev_exit_loss(fake, 1, fake, fake, fake, 2, 9, 4, 1000, fake, fake, fake, null, fake, need_l - 1, s) == 5
+    # tree builder
+    need_t = L.tev_build_tree_workspace_bytes(1, 16, 151936, 64)
+    assert need_t > 0
+    assert L.tev_build_tree_workspace_bytes(1, 17, 151936, 64) == 0       # L > 16
+    assert L.tev_build_tree_workspace_bytes(1, 16, 151936, 129) == 0      # K > 128
+    assert L.tev_build_tree_workspace_bytes(1, 16, 600000, 8) == 0        # more than 64 slabs
+    assert L.tev_build_tree(null, 1, null, 1, 16, 151936, 64, 64, fake, fake, fake, fake, need_t, s) == 1
+    assert L.tev_build_tree(fake, 1, null, 1, 2, 151936, 3, 14, fake, fake, fake, fake, need_t, s) == 2  # 3 + 9 < 13
+    assert L.tev_build_tree(fake, 1, null, 1, 16, 151936, 64, 257, fake, fake, fake, fake, need_t, s) == 2
+    assert L.tev_build_tree(fake, 1, null, 1, 16, 151936, 64, 64, fake, fake, fake, fake, need_t - 1, s) == 5
     # exports
     assert L.tev_export_residual_cdf(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, need, 1, 0, fake, s) == 2
     assert L.tev_read_device_status(null, 0, 1, 4, 10, fake, s) == 1

@@ -1,0 +1,153 @@
+"""GPU parity of tev_build_tree (best-first draft tree over the top-K retained
+universe, "CAST" App. C "Candidate construction" / Thm. 1, "Multi-Future
+Drafting" App. B with one mode) against the oracle, through the C ABI.
+
+Both sides order prefixes by the same key, sum of logits along the path (f64,
+the same additions in the same order) minus the sum of the row logsumexps of
+its depths, so equal keys are equal on both sides and the tree is compared
+node for node.  The row logsumexps differ in their last bits (the GPU sums
+exp in f64 slab by slab); where the oracle sees two keys within 1e-9 of each
+other that do not come from identical logit sums (a coincidental near tie),
+either order is correct, and the test checks instead that the GPU tree is a
+valid top set: a tree of retained tokens whose node scores, sorted, equal the
+oracle's to 1e-9 and come out best first.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_tree_verification_amd import tev
+from draft_tree_verification_amd import workloads as W
+from tests import gpu_parity as GP
+
+pytestmark = pytest.mark.gpu
+
+SCORE_ABS = 1e-9
+
+
+def _gpu(z, dtype, K, B, roots):
+    res = tev.tev_build_tree(tev.to_device_logits(z, dtype), K, B, tev.to_device_i32(roots))
+    torch.cuda.synchronize()
+    return (res.parents.cpu().numpy(), res.tokens.cpu().numpy(), res.scores.cpu().numpy(), res)
+
+
+def _widen(z, dtype):
+    if dtype == "bf16":
+        return (z.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return z.astype(np.float64)
+
+
+def _check_valid_top_set(z64, K, B, par, tok, sc, ref_scores):
+    """The GPU tree is a tree of retained tokens with distinct siblings, its
+    scores are the oracle's scores of the same paths, best first, and as a
+    set they are the oracle's top B - 1 scores."""
+    L, V = z64.shape
+    lse = np.array([np.logaddexp.reduce(z64[j]) for j in range(L)])
+    keep = [set(np.lexsort((np.arange(V), -z64[j]))[:K].tolist()) for j in range(L)]
+    depth = np.zeros(B, int)
+    path_sum = np.zeros(B)
+    seen = set()
+    for i in range(1, B):
+        p = par[i]
+        assert 0 <= p < i
+        depth[i] = depth[p] + 1
+        assert depth[i] <= L and int(tok[i]) in keep[depth[i] - 1]
+        assert (p, int(tok[i])) not in seen
+        seen.add((p, int(tok[i])))
+        path_sum[i] = path_sum[p] + z64[depth[i] - 1, tok[i]] - lse[depth[i] - 1]
+    np.testing.assert_allclose(sc[1:], path_sum[1:], rtol=0, atol=1e-8)
+    assert np.all(np.diff(sc[1:]) <= SCORE_ABS)
+    np.testing.assert_allclose(np.sort(sc[1:]), np.sort(ref_scores[1:]), rtol=0, atol=1e-8)
+
+
+def _compare(z, dtype, K, B, seed=0):
+    R = z.shape[0]
+    roots = np.random.default_rng(seed).integers(0, z.shape[2], size=R).astype(np.int32)
+    par, tok, sc, res = _gpu(z, dtype, K, B, roots)
+    ref = oracle.build_tree(z, dtype, K, B, roots, tie_eps=SCORE_ABS)
+    assert not np.any(tev.tev_read_device_status(res.workspace, 4, R))
+    exact = 0
+    for r in range(R):
+        if not ref.near_tie[r]:
+            np.testing.assert_array_equal(par[r], ref.parents[r])
+            np.testing.assert_array_equal(tok[r], ref.tokens[r])
+            np.testing.assert_allclose(sc[r], ref.scores[r], rtol=0, atol=SCORE_ABS)
+            exact += 1
+        else:
+            assert tok[r, 0] == roots[r] and par[r, 0] == -1
+            _check_valid_top_set(_widen(z[r], dtype), K, B, par[r], tok[r], sc[r], ref.scores[r])
+    return exact
+
+
+CASES = [
+    dict(R=2, L=4, V=1000, K=8, B=40, dtype="f32"),
+    dict(R=3, L=16, V=20000, K=64, B=64, dtype="f32"),
+    dict(R=1, L=6, V=8193, K=128, B=256, dtype="f32"),      # a one-logit last slab
+    dict(R=2, L=3, V=777, K=16, B=200, dtype="f32"),         # rows not 16-byte multiples
+    dict(R=2, L=5, V=1001, K=32, B=100, dtype="bf16"),
+    dict(R=4, L=16, V=40000, K=1, B=17, dtype="bf16"),       # top-1: the argmax chain
+    dict(R=1, L=1, V=5000, K=100, B=101, dtype="f32"),       # one position: a star of the top 100
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"R{c['R']}_L{c['L']}_V{c['V']}_K{c['K']}_B{c['B']}_{c['dtype']}")
+def test_build_tree_matches_oracle(case):
+    GP.log(f"[build_tree] {case}")
+    rng = np.random.default_rng(case["V"] + case["K"])
+    z = (rng.standard_normal((case["R"], case["L"], case["V"])) * 3.0).astype(np.float32)
+    if case["dtype"] == "bf16":
+        z = W.f32_to_bf16_bits(z)
+    exact = _compare(z, case["dtype"], case["K"], case["B"])
+    assert exact >= 1
+
+
+def test_equal_logits_tie_order():
+    """All logits equal: every prefix of a depth ties; order by depth, then
+    rank sequence, ranks by token id (the oracle's closed form)."""
+    z = np.zeros((1, 3, 10), np.float32)
+    par, tok, sc, _ = _gpu(z, "f32", 3, 18, np.array([0], np.int32))
+    np.testing.assert_array_equal(par[0], [-1, 0, 0, 0, 1, 1, 1, 2, 2, 2, 3, 3, 3, 4, 4, 4, 5, 5])
+    np.testing.assert_array_equal(tok[0], [0, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1])
+
+
+def test_heavy_bf16_ties():
+    """bf16 logits on a coarse grid: many tokens share a logit, so ranks are
+    decided by token id and many prefixes tie exactly."""
+    rng = np.random.default_rng(3)
+    z = np.round(rng.standard_normal((3, 8, 30000)) * 2).astype(np.float32)
+    _compare(W.f32_to_bf16_bits(z), "bf16", 48, 128)
+
+
+@pytest.mark.parametrize("name,K,B", [("qwen3_4b", 64, 64), ("qwen3_8b_wide", 128, 128),
+                                      ("batched", 64, 64)])
+def test_named_workload_draft_rows(name, K, B):
+    """The trees of the named workloads' own draft rows (V = 151936 bf16, 16
+    positions), K = B tokens kept per position as their builder does."""
+    z = W.draft_rows(name)
+    GP.log(f"[build_tree] {name} R={z.shape[0]} L={z.shape[1]} V={z.shape[2]} K={K} B={B}")
+    exact = _compare(z, "bf16", K, B)
+    assert exact >= 1
+
+
+def test_non_finite_rows_are_flagged():
+    rng = np.random.default_rng(9)
+    z = (rng.standard_normal((3, 4, 9000)) * 2).astype(np.float32)
+    z[1, 2, 4444] = np.nan
+    z[2, 0, :] = -np.inf
+    roots = np.zeros(3, np.int32)
+    par, tok, sc, res = _gpu(z, "f32", 8, 30, roots)
+    flags = tev.tev_read_device_status(res.workspace, 4, 3)
+    np.testing.assert_array_equal(flags != 0, [False, True, True])
+    assert np.all(tok[1:] == -1) and np.all(par[1:] == -1) and np.all(np.isnan(sc[1:]))
+    ref = oracle.build_tree(z[:1], "f32", 8, 30, roots[:1])
+    np.testing.assert_array_equal(par[0], ref.parents[0])
+    np.testing.assert_array_equal(tok[0], ref.tokens[0])
+
+
+def test_repeat_is_bit_identical():
+    z = W.f32_to_bf16_bits((np.random.default_rng(12).standard_normal((2, 16, 50000)) * 4).astype(np.float32))
+    a = _gpu(z, "bf16", 32, 96, np.zeros(2, np.int32))
+    b = _gpu(z, "bf16", 32, 96, np.zeros(2, np.int32))
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
