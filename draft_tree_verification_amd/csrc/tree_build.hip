@@ -17,21 +17,20 @@
 // Launches:
 //   k_tb_slabs  grid (ns, R*L), 256 threads: one 8192-logit slab in registers;
 //               slab maximum and f64 sum of exp(z - maximum); the slab's K
-//               best keys, best first.  The K-th largest per-thread maximum
-//               bounds the slab's K-th key from below, so only keys at or
-//               above it (at most 32 K) go to LDS, where each is ranked by
-//               counting.  key = (order-preserving bits of z) << 32 | ~token,
+//               best keys, best first (block_top_k).  key = (order-preserving
+//               bits of z) << 32 | ~token,
 //               unique per token, so "larger logit, then smaller token" is one
 //               unsigned comparison.
-//   k_tb_rows   grid R*L, 256 threads: the row's slab lists in LDS; the largest
-//               K-th entry over the lists bounds the row's K-th key from below;
-//               each key at or above it is ranked by a binary search in every
-//               list.  Writes the row's top K and its logsumexp (f64).
+//   k_tb_rows   grid R*L, 256 threads: the union of the row's slab lists, 32
+//               keys per thread, through the same selection; writes the row's
+//               top K and its logsumexp (f64).
 //   k_tb_heap   grid R, one wave: the best-first search.  The frontier sits in
-//               registers (4 slots per lane; it never holds more than B
-//               entries); each pop is one wave maximum over the keys (ties
-//               settled by depth and rank sequence), emits a node and pushes
-//               its next sibling and its first child.
+//               registers, one slot per node holding that node's next child
+//               (ceil(B / 64) slots per lane); each pop is one DPP wave
+//               maximum over the keys in f32 with the exact order settled
+//               among the lanes that reach it, records a node, moves the
+//               winner's slot to the next sibling and opens the new node's
+//               slot with its rank-0 child.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -68,6 +67,72 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     return x;
 }
 
+// The K best of the keys the workgroup holds, N per thread (0 = no key),
+// written best first to out[0..K) (0 past the last key).  The K-th largest
+// per-thread maximum bounds the K-th key from below (K threads hold a key at
+// least that large), so only keys at or above it -- at most N K of them, from
+// those K threads -- are compacted into LDS, where each is ranked by counting
+// the larger ones.  Keys are unique, so the ranks are distinct.
+template <int N>
+__device__ __forceinline__ void block_top_k(const uint64_t (&key)[N], int K, uint64_t *s_c,
+                                            uint64_t *s_tmax, int *s_cnt, uint64_t *s_tau,
+                                            uint64_t *out) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint64_t tmax = 0ull;
+#pragma unroll
+    for (int j = 0; j < N; j++) tmax = key[j] > tmax ? key[j] : tmax;
+    s_tmax[tid] = tmax;
+    if (tid == 0) *s_tau = 1ull;
+    __syncthreads();
+    // in batches of 16 broadcast reads, all issued before the first compare
+    int rank = 0;
+    for (int j = 0; j < TB_THREADS; j += 16) {
+        uint64_t t[16];
+#pragma unroll
+        for (int u = 0; u < 16; u++) t[u] = s_tmax[j + u];
+#pragma unroll
+        for (int u = 0; u < 16; u++) rank += t[u] > tmax ? 1 : 0;
+    }
+    if (rank == K - 1 && tmax != 0ull) *s_tau = tmax;
+    __syncthreads();
+    const uint64_t tau = *s_tau;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; j++) cnt += key[j] >= tau ? 1 : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_cnt[wv] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
+    for (int w = 0; w < wv; w++) pos += s_cnt[w];
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < TB_THREADS / 64; w++) n += s_cnt[w];
+#pragma unroll
+    for (int j = 0; j < N; j++)
+        if (key[j] >= tau) s_c[pos++] = key[j];
+    const int n16 = (n + 15) & ~15;                   // zero padding: never above a key
+    for (int i = n + tid; i < n16; i += TB_THREADS) s_c[i] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < n; i += TB_THREADS) {
+        const uint64_t c = s_c[i];
+        int r = 0;
+        for (int j = 0; j < n16; j += 16) {
+            uint64_t t[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) t[u] = s_c[j + u];
+#pragma unroll
+            for (int u = 0; u < 16; u++) r += t[u] > c ? 1 : 0;
+        }
+        if (r < K) out[r] = c;
+    }
+    for (int i = n + tid; i < K; i += TB_THREADS) out[i] = 0ull;
+}
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z, int V, int ns, int K,
                                                          unsigned *__restrict__ flag,
@@ -77,7 +142,7 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
     constexpr int VW = 16 / (int)sizeof(T);
     constexpr int SPAN = TB_THREADS * VW;
     constexpr int NWV = TB_THREADS / 64;
-    extern __shared__ uint64_t s_cand[];             // at most TB_EPT * K keys
+    extern __shared__ uint64_t s_c[];                 // TB_EPT * K keys + 16 of padding
     __shared__ uint64_t s_tmax[TB_THREADS];
     __shared__ float s_max[NWV];
     __shared__ double s_sum[NWV];
@@ -90,22 +155,13 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
     load_slab<T, VEC, TB_THREADS, TB_EPT>(z + m * (size_t)V + start, len, tid, x);
     bool bad = false;
     float mx = -kInf;
-    uint64_t tmax = 0;
 #pragma unroll
-    for (int k = 0; k < TB_EPT / VW; k++)
-#pragma unroll
-        for (int j = 0; j < VW; j++) {
-            const float v = x[k * VW + j];
-            const int idx = k * SPAN + tid * VW + j;
-            bad |= (v != v) | (v == kInf);
-            mx = fmaxf(mx, v);
-            const uint64_t key = idx < len ? make_key(v, start + idx) : 0ull;
-            tmax = key > tmax ? key : tmax;
-        }
+    for (int j = 0; j < TB_EPT; j++) {
+        bad |= (x[j] != x[j]) | (x[j] == kInf);
+        mx = fmaxf(mx, x[j]);
+    }
     mx = wave::max_f32(mx);
     if (lane == 0) s_max[wv] = mx;
-    s_tmax[tid] = tmax;
-    if (tid == 0) s_tau = 1ull;
     const int any_bad = __syncthreads_or(bad);
     mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     double acc = 0.0;
@@ -115,48 +171,15 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
     }
     acc = wave::sum_f64(acc);
     if (lane == 0) s_sum[wv] = acc;
-    // the thread whose maximum ranks K-th sets the bound (keys are unique)
-    int rank = 0;
-    for (int j = 0; j < TB_THREADS; j++) rank += s_tmax[j] > tmax;
-    if (rank == K - 1 && tmax != 0ull) s_tau = tmax;
-    __syncthreads();
-    const uint64_t tau = s_tau;
-    int cnt = 0;
+    uint64_t key[TB_EPT];
 #pragma unroll
     for (int k = 0; k < TB_EPT / VW; k++)
 #pragma unroll
         for (int j = 0; j < VW; j++) {
             const int idx = k * SPAN + tid * VW + j;
-            cnt += (idx < len && make_key(x[k * VW + j], start + idx) >= tau) ? 1 : 0;
+            key[k * VW + j] = idx < len ? make_key(x[k * VW + j], start + idx) : 0ull;
         }
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_cnt[wv] = incl;
-    __syncthreads();
-    int pos = incl - cnt;
-    for (int w = 0; w < wv; w++) pos += s_cnt[w];
-    const int n = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-#pragma unroll
-    for (int k = 0; k < TB_EPT / VW; k++)
-#pragma unroll
-        for (int j = 0; j < VW; j++) {
-            const int idx = k * SPAN + tid * VW + j;
-            const uint64_t key = idx < len ? make_key(x[k * VW + j], start + idx) : 0ull;
-            if (idx < len && key >= tau) s_cand[pos++] = key;
-        }
-    __syncthreads();
-    uint64_t *out = cand + (m * ns + s) * (size_t)K;
-    for (int i = tid; i < n; i += TB_THREADS) {
-        const uint64_t c = s_cand[i];
-        int r = 0;
-        for (int j = 0; j < n; j++) r += s_cand[j] > c;
-        if (r < K) out[r] = c;
-    }
-    for (int i = n + tid; i < K; i += TB_THREADS) out[i] = 0ull;   // a short slab: no more keys
+    block_top_k<TB_EPT>(key, K, s_c, s_tmax, s_cnt, &s_tau, cand + (m * ns + s) * (size_t)K);
     if (tid == 0) {
         slab_m[m * ns + s] = mx;
         slab_s[m * ns + s] = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
@@ -164,18 +187,29 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
     }
 }
 
+// One row: the union of its slab lists (ns K <= 8192 keys, 32 per thread) and
+// the row's logsumexp from the slab partials.
 __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restrict__ flag,
                                                         const float *__restrict__ slab_m,
                                                         const double *__restrict__ slab_s,
                                                         const uint64_t *__restrict__ cand, int ns, int K,
                                                         uint64_t *__restrict__ top, double *__restrict__ lse,
                                                         unsigned *__restrict__ row_flag) {
-    extern __shared__ uint64_t s_list[];              // ns lists of K keys, each best first
-    __shared__ uint64_t s_bound;
+    constexpr int NWV = TB_THREADS / 64;
+    constexpr int NK = 8192 / TB_THREADS;
+    extern __shared__ uint64_t s_c[];                 // NK * K keys + 16 of padding
+    __shared__ uint64_t s_tmax[TB_THREADS];
+    __shared__ int s_cnt[NWV];
+    __shared__ uint64_t s_tau;
     const int tid = threadIdx.x, lane = tid & 63;
     const size_t m = blockIdx.x;
     const int nk = ns * K;
-    for (int i = tid; i < nk; i += TB_THREADS) s_list[i] = cand[m * (size_t)nk + i];
+    uint64_t key[NK];
+#pragma unroll
+    for (int j = 0; j < NK; j++) {
+        const int i = j * TB_THREADS + tid;
+        key[j] = i < nk ? cand[m * (size_t)nk + i] : 0ull;
+    }
     if (tid < 64) {
         // the row's logsumexp from the slab partials (ns <= 64: one per lane)
         float ms = -kInf;
@@ -197,35 +231,7 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restri
             row_flag[m] = (any || !(l > -(double)kInf && l < (double)kInf)) ? (unsigned)TEV_FLAG_NONFINITE : 0u;
         }
     }
-    __syncthreads();
-    if (tid < 64) {
-        uint64_t b = 1ull;
-        for (int s = lane; s < ns; s += 64) {
-            const uint64_t e = s_list[s * K + K - 1];
-            b = e > b ? e : b;
-        }
-        b = wave_max_u64(b);
-        if (lane == 0) s_bound = b;
-    }
-    __syncthreads();
-    const uint64_t bound = s_bound;
-    uint64_t *o = top + m * (size_t)K;
-    for (int i = tid; i < nk; i += TB_THREADS) {
-        const uint64_t c = s_list[i];
-        if (c < bound) continue;
-        // rank = number of keys above c: a binary search in every sorted list
-        int r = 0;
-        for (int s = 0; s < ns; s++) {
-            const uint64_t *l = s_list + s * K;
-            int lo = 0, hi = K;                         // first index whose key is <= c
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (l[mid] > c) lo = mid + 1; else hi = mid;
-            }
-            r += lo;
-        }
-        if (r < K) o[r] = c;
-    }
+    block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, &s_tau, top + m * (size_t)K);
 }
 
 // The rank of depth d (1-based) packed big-endian: depths 1..8 in hi, 9..16 in lo.
@@ -242,14 +248,20 @@ __device__ __forceinline__ void set_rank(uint64_t &hi, uint64_t &lo, int d, int 
     }
 }
 
-struct Entry {
-    double s, sz;
-    uint64_t hi, lo;
-    int depth, parent;      // depth 0: empty slot
+// Frontier slots.  Slot p (lane p mod 64, register p / 64) belongs to node
+// p and holds the next not yet emitted child of p: first its rank-0 child,
+// then, each time that child is popped, the next sibling.  So a pop changes
+// only the winner's own slot and the new node's slot, no slot is searched
+// for, and the parent of a slot's entry is the slot's node.
+struct Slot {
+    double s, sz, psz;      // key, logit sum of the path, logit sum of the parent's path
+    uint64_t hi, lo;        // rank sequence, depth d in byte d (big-endian, hi then lo)
+    float zn;               // logit of the next sibling's token (NaN: no next sibling)
+    int depth;              // 0: empty
 };
 
 // a before b in pop order: larger key, then shorter, then smaller rank sequence
-__device__ __forceinline__ bool before(const Entry &a, const Entry &b) {
+__device__ __forceinline__ bool before(const Slot &a, const Slot &b) {
     if (a.depth == 0) return false;
     if (b.depth == 0) return true;
     if (a.s != b.s) return a.s > b.s;
@@ -258,147 +270,163 @@ __device__ __forceinline__ bool before(const Entry &a, const Entry &b) {
     return a.lo < b.lo;
 }
 
-__device__ __forceinline__ Entry readlane_entry(const Entry &e, int l) {
-    Entry o;
-    o.s = wave::readlane_d(e.s, l);
-    o.sz = wave::readlane_d(e.sz, l);
-    o.hi = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(e.hi >> 32), l) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)e.hi, l);
-    o.lo = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(e.lo >> 32), l) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)e.lo, l);
-    o.depth = __builtin_amdgcn_readlane(e.depth, l);
-    o.parent = __builtin_amdgcn_readlane(e.parent, l);
-    return o;
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
 }
 
-constexpr int SLOTS = 4;    // frontier slots per lane: 256 entries >= B
-
+// One wave per request; SLOTS = ceil(B / 64) slots per lane.
+template <int SLOTS>
 __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top, const double *__restrict__ lse,
                                                 const unsigned *__restrict__ row_flag,
                                                 const int32_t *__restrict__ root_tokens, int L, int K, int B,
                                                 unsigned *__restrict__ status, int32_t *__restrict__ parents,
                                                 int32_t *__restrict__ tokens, double *__restrict__ scores) {
-    __shared__ double s_tz[TB_MAX_L * TB_MAX_K];
+    constexpr int NLD = TB_MAX_L * TB_MAX_K / 64;     // top-K entries per lane
+    __shared__ float s_tz[TB_MAX_L * TB_MAX_K];
     __shared__ int s_tt[TB_MAX_L * TB_MAX_K];
-    __shared__ double s_C[TB_MAX_L + 1];
-    __shared__ double s_nsz[TEV_MAX_NODES];
+    __shared__ int s_par[TEV_MAX_NODES], s_idx[TEV_MAX_NODES];
+    __shared__ double s_sc[TEV_MAX_NODES];
     const int lane = threadIdx.x, r = blockIdx.x;
-    unsigned fl = 0u;
-    for (int i = lane; i < L * K; i += 64) {
-        const uint64_t key = top[(size_t)r * L * K + i];
-        s_tz[i] = (double)unord32((uint32_t)(key >> 32));
-        s_tt[i] = (int)~(uint32_t)key;
+    const float qnan = __builtin_nanf("");
+    // every load first, then the LDS stores
+    const int LK = L * K;
+    uint64_t kv[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; j++) {
+        const int i = j * 64 + lane;
+        kv[j] = i < LK ? top[(size_t)r * LK + i] : 0ull;
     }
-    for (int j = lane; j < L; j += 64) fl |= row_flag[(size_t)r * L + j];
-    fl = (unsigned)wave::sum_i32((int)fl) != 0u ? (unsigned)TEV_FLAG_NONFINITE : 0u;
-    if (lane == 0) {
-        double c = 0.0;                                 // C[d] = lse_0 + ... + lse_{d-1}, in order
-        s_C[0] = 0.0;
-        for (int j = 0; j < L; j++) {
-            c += lse[(size_t)r * L + j];
-            s_C[j + 1] = c;
+    const double lse_l = lane < L ? lse[(size_t)r * L + lane] : 0.0;
+    const unsigned rf = lane < L ? row_flag[(size_t)r * L + lane] : 0u;
+#pragma unroll
+    for (int j = 0; j < NLD; j++) {
+        const int i = j * 64 + lane;
+        if (i < LK) {
+            s_tz[i] = unord32((uint32_t)(kv[j] >> 32));
+            s_tt[i] = (int)~(uint32_t)kv[j];
         }
-        s_nsz[0] = 0.0;
-        status[r] = fl;
-        parents[(size_t)r * B] = -1;
-        tokens[(size_t)r * B] = fl ? -1 : (root_tokens ? root_tokens[r] : 0);
-        scores[(size_t)r * B] = fl ? __builtin_nan("") : 0.0;
+    }
+    const unsigned fl = __ballot(rf != 0u) != 0ull ? (unsigned)TEV_FLAG_NONFINITE : 0u;
+    // lane d holds C[d] = lse_0 + ... + lse_{d-1} (summed in order), and the
+    // rank-0 and rank-1 logits of depth d (position d)
+    double creg = 0.0, c = 0.0;
+    for (int j = 0; j < L; j++) {
+        c += wave::readlane_d(lse_l, j);
+        if (lane == j + 1) creg = c;
     }
     __syncthreads();
+    const float zr0 = (lane >= 1 && lane <= L) ? s_tz[(lane - 1) * K] : qnan;
+    const float zr1 = (lane >= 1 && lane <= L && K > 1) ? s_tz[(lane - 1) * K + 1] : qnan;
+    if (lane == 0) status[r] = fl;
     if (fl) {
-        for (int n = 1 + lane; n < B; n += 64) {
+        for (int n = lane; n < B; n += 64) {
             parents[(size_t)r * B + n] = -1;
             tokens[(size_t)r * B + n] = -1;
             scores[(size_t)r * B + n] = __builtin_nan("");
         }
         return;
     }
-    Entry f[SLOTS];
+    Slot f[SLOTS];
 #pragma unroll
-    for (int q = 0; q < SLOTS; q++) f[q] = Entry{0.0, 0.0, 0ull, 0ull, 0, 0};
-    if (B > 1 && lane == 0) {                            // the rank-0 token of position 1
-        f[0].sz = s_tz[0];
-        f[0].s = f[0].sz - s_C[1];
-        f[0].depth = 1;
+    for (int q = 0; q < SLOTS; q++) f[q] = Slot{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
+    {   // the root's slot: its rank-0 child at position 1
+        const double sz = (double)wave::readlane_f(zr0, 1);
+        if (lane == 0) {
+            f[0].sz = sz;
+            f[0].s = sz - wave::readlane_d(creg, 1);
+            f[0].zn = wave::readlane_f(zr1, 1);
+            f[0].depth = 1;
+        }
     }
-    for (int n = 1; n < B; n++) {
-        // the lane's best slot
+    int n = 1;
+    for (; n < B; n++) {
         int bq = 0;
-        Entry mine = f[0];
+        Slot mine = f[0];
 #pragma unroll
         for (int q = 1; q < SLOTS; q++)
             if (before(f[q], mine)) {
                 mine = f[q];
                 bq = q;
             }
-        const uint64_t o = mine.depth ? ord64(mine.s) : 0ull;
-        const uint64_t best = wave_max_u64(o);
-        uint64_t ball = __ballot(o == best && mine.depth != 0);
-        if (ball == 0ull) {                              // the universe is exhausted
-            for (int i = n + lane; i < B; i += 64) {
-                parents[(size_t)r * B + i] = -1;
-                tokens[(size_t)r * B + i] = -1;
-                scores[(size_t)r * B + i] = __builtin_nan("");
-            }
-            break;
-        }
+        // coarse maximum in f32 (monotone rounding keeps the true maximum
+        // among the lanes that reach it), then the exact order among those
+        const float k32 = mine.depth ? (float)mine.s : -kInf;
+        const float m32 = wave::max_f32(k32);
+        uint64_t ball = __ballot(mine.depth != 0 && k32 == m32);
+        if (ball == 0ull) break;                         // the universe is exhausted
         int wl = __ffsll((long long)ball) - 1;
-        Entry w = readlane_entry(mine, wl);
         ball &= ball - 1;
-        while (ball) {                                   // equal keys: depth, then rank sequence
-            const int l = __ffsll((long long)ball) - 1;
-            ball &= ball - 1;
-            const Entry e = readlane_entry(mine, l);
-            if (before(e, w)) {
-                w = e;
-                wl = l;
+        if (ball) {
+            Slot w;
+            w.s = wave::readlane_d(mine.s, wl);
+            w.hi = readlane_u64(mine.hi, wl);
+            w.lo = readlane_u64(mine.lo, wl);
+            w.depth = __builtin_amdgcn_readlane(mine.depth, wl);
+            while (ball) {
+                const int l = __ffsll((long long)ball) - 1;
+                ball &= ball - 1;
+                Slot e;
+                e.s = wave::readlane_d(mine.s, l);
+                e.hi = readlane_u64(mine.hi, l);
+                e.lo = readlane_u64(mine.lo, l);
+                e.depth = __builtin_amdgcn_readlane(mine.depth, l);
+                if (before(e, w)) {
+                    w = e;
+                    wl = l;
+                }
             }
         }
-        // emit node n
-        const int d = w.depth;
-        const int rk = rank_at(w.hi, w.lo, d);
+        const double ws = wave::readlane_d(mine.s, wl);
+        const double wsz = wave::readlane_d(mine.sz, wl);
+        const uint64_t whi = readlane_u64(mine.hi, wl), wlo = readlane_u64(mine.lo, wl);
+        const int d = __builtin_amdgcn_readlane(mine.depth, wl);
+        const int wq = __builtin_amdgcn_readlane(bq, wl);
+        const int rk = rank_at(whi, wlo, d);
+        const int parent = wq * 64 + wl;                 // the slot's node
         if (lane == 0) {
-            parents[(size_t)r * B + n] = w.parent;
-            tokens[(size_t)r * B + n] = s_tt[(d - 1) * K + rk];
-            scores[(size_t)r * B + n] = w.s;
-            s_nsz[n] = w.sz;
+            s_par[n] = parent;
+            s_idx[n] = (d - 1) * K + rk;
+            s_sc[n] = ws;
         }
-        // the winner's slot takes the next sibling (or empties)
-        Entry sib{0.0, 0.0, 0ull, 0ull, 0, 0};
-        if (rk + 1 < K) {
-            sib.sz = s_nsz[w.parent] + s_tz[(d - 1) * K + rk + 1];
-            sib.s = sib.sz - s_C[d];
-            sib.hi = w.hi;
-            sib.lo = w.lo;
-            set_rank(sib.hi, sib.lo, d, rk + 1);
-            sib.depth = d;
-            sib.parent = w.parent;
-        }
+        // the winner's slot moves on to the next sibling (or empties)
         if (lane == wl) {
+            Slot sib{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
+            if (rk + 1 < K) {
+                sib.psz = mine.psz;
+                sib.sz = mine.psz + (double)mine.zn;
+                sib.s = sib.sz - wave::readlane_d(creg, d);
+                sib.hi = whi;
+                sib.lo = wlo;
+                set_rank(sib.hi, sib.lo, d, rk + 1);
+                sib.zn = rk + 2 < K ? s_tz[(d - 1) * K + rk + 2] : qnan;
+                sib.depth = d;
+            }
 #pragma unroll
             for (int q = 0; q < SLOTS; q++)
                 if (q == bq) f[q] = sib;
         }
-        // the first child goes to the first free slot of the first lane with one
-        if (d < L) {
-            Entry ch;
-            ch.sz = w.sz + s_tz[d * K];
-            ch.s = ch.sz - s_C[d + 1];
-            ch.hi = w.hi;
-            ch.lo = w.lo;                                // rank 0 at depth d + 1: byte already 0
+        // node n's slot starts with its rank-0 child
+        if (d < L && lane == (n & 63)) {
+            Slot ch;
+            ch.psz = wsz;
+            ch.sz = wsz + (double)wave::readlane_f(zr0, d + 1);
+            ch.s = ch.sz - wave::readlane_d(creg, d + 1);
+            ch.hi = whi;                                  // rank 0 at depth d + 1: byte already 0
+            ch.lo = wlo;
+            ch.zn = wave::readlane_f(zr1, d + 1);
             ch.depth = d + 1;
-            ch.parent = n;
-            int fq = -1;
 #pragma unroll
-            for (int q = SLOTS - 1; q >= 0; q--)
-                if (f[q].depth == 0) fq = q;
-            const uint64_t fb = __ballot(fq >= 0);
-            if (lane == __ffsll((long long)fb) - 1) {
-#pragma unroll
-                for (int q = 0; q < SLOTS; q++)
-                    if (q == fq) f[q] = ch;
-            }
+            for (int q = 0; q < SLOTS; q++)
+                if (q == (n >> 6)) f[q] = ch;
         }
+    }
+    __syncthreads();
+    for (int i = lane; i < B; i += 64) {
+        const bool ok = i == 0 || i < n;
+        parents[(size_t)r * B + i] = i == 0 ? -1 : (ok ? s_par[i] : -1);
+        tokens[(size_t)r * B + i] = i == 0 ? (root_tokens ? root_tokens[r] : 0) : (ok ? s_tt[s_idx[i]] : -1);
+        scores[(size_t)r * B + i] = i == 0 ? 0.0 : (ok ? s_sc[i] : (double)qnan);
     }
 }
 
@@ -414,12 +442,17 @@ hipError_t launch_typed(const void *z, const int32_t *root_tokens, int R, int L,
     uint64_t *top = (uint64_t *)(ws + W.top);
     double *lse = (double *)(ws + W.lse);
     unsigned *row_flag = (unsigned *)(ws + W.row_flag);
-    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(R * L)), TB_THREADS, (size_t)TB_EPT * K * 8, st>>>(
+    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(R * L)), TB_THREADS, ((size_t)TB_EPT * K + 16) * 8, st>>>(
         static_cast<const T *>(z), V, ns, K, flag, slab_m, slab_s, cand);
-    k_tb_rows<<<R * L, TB_THREADS, (size_t)ns * K * 8, st>>>(flag, slab_m, slab_s, cand, ns, K, top, lse,
-                                                             row_flag);
-    k_tb_heap<<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, (unsigned *)(ws + W.status),
-                                parents, tokens, scores);
+    k_tb_rows<<<R * L, TB_THREADS, ((size_t)(8192 / TB_THREADS) * K + 16) * 8, st>>>(flag, slab_m, slab_s, cand, ns, K,
+                                                                            top, lse, row_flag);
+    unsigned *status = (unsigned *)(ws + W.status);
+    switch ((B + 63) / 64) {
+    case 1: k_tb_heap<1><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
+    case 2: k_tb_heap<2><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
+    case 3: k_tb_heap<3><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
+    default: k_tb_heap<4><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
+    }
     return hipGetLastError();
 }
 
