@@ -15,7 +15,8 @@ arrays.  Sources:
   App. B Algorithm 1 (TEV's two draws), Sec. 5 Eq. 14 (the exit-guided
   draft-tree loss, ``exit_loss``).
 * "CAST" App. C "Candidate construction" and "Multi-Future Drafting" App. B
-  (the best-first tree builder, ``build_tree``).
+  (the best-first tree builder, ``build_tree``; the merged heap over several
+  draft modes, ``build_tree_modes``).
 * "CAST: Cost-Aware Speculative Trees from One-Pass Block Drafters"
   (arXiv 2610.00321): App. B Lemma 1 and App. C "Packed verification"
   (ancestor-only attention mask).
@@ -381,6 +382,97 @@ def build_tree(draft_logits: np.ndarray, dtype: str, topk: int, n_nodes: int,
         keys_seen.sort()
         for (s1, z1, d1), (s2, z2, d2) in zip(keys_seen, keys_seen[1:]):
             if s2 - s1 <= tie_eps and not (z1 == z2 and d1 == d2):
+                near[r] = True
+                break
+    return BuiltTree(par, tok, sc, near)
+
+
+def build_tree_modes(draft_logits: np.ndarray, dtype: str, topk: int, n_nodes: int,
+                     root_tokens: np.ndarray, log_prior: np.ndarray | None = None,
+                     tie_eps: float = 1e-9) -> BuiltTree:
+    """The merged heap over several draft modes ("Multi-Future Drafting",
+    App. B, Prop. 6): the tree of the n_nodes - 1 distinct prefixes with the
+    largest best-mode score s(v) = max_k s_k(v), in the order of their first
+    pops.
+
+    draft_logits [R][M][L][V]: mode k's position-wise logits.  log_prior
+    [R][M] (log pi_k; uniform -log M when None).  Mode k's key of a prefix of
+    its retained universe (its own top-K tokens per position) is
+        s_k(v) = ((sum_j z_{k,j,y_j}) - (sum_j lse_{k,j})) + log pi_k
+    (the single-mode key of ``build_tree`` plus the log prior).  The heap holds
+    entries (k, v) keyed by s_k(v) and starts from every mode's rank-0 token
+    of position 1; popping (k, v) adds a node for v unless the tree holds it
+    already, and pushes v's next sibling and first child under mode k either
+    way.  Equal keys go to the shorter prefix, then the smaller rank sequence,
+    then the smaller mode.  With one mode and no prior this is ``build_tree``.
+    If the modes' universes hold fewer than n_nodes - 1 distinct prefixes, the
+    missing nodes get parent and token -1 and score NaN.
+
+    near_tie[r] as in ``build_tree``, over every popped entry and every entry
+    left in the heap (keys computed from identical logit sums, logsumexp sums
+    and priors are exact ties on both sides and are not reported)."""
+    z = _as_input(draft_logits, dtype)
+    if dtype == "bf16":
+        z = (z.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    z = z.astype(np.float64)
+    R, M, L, V = z.shape
+    if not (1 <= topk <= V) or n_nodes < 1:
+        raise OracleError("bad topk / n_nodes")
+    if n_nodes - 1 > M * sum(topk ** d for d in range(1, L + 1)):
+        raise OracleError("the retained universes hold fewer prefixes than n_nodes - 1")
+    lp = (np.full((R, M), -np.log(M)) if log_prior is None
+          else np.asarray(log_prior, dtype=np.float32).astype(np.float64).reshape(R, M))
+    if M == 1 and log_prior is None:
+        lp[:] = 0.0
+    par = np.full((R, n_nodes), -1, np.int32)
+    tok = np.zeros((R, n_nodes), np.int32)
+    sc = np.zeros((R, n_nodes))
+    near = np.zeros(R, bool)
+    for r in range(R):
+        C, order, ztop = [], [], []
+        for k in range(M):
+            lse = np.array([_logsumexp64(z[r, k, j]) for j in range(L)])
+            C.append(np.concatenate([[0.0], np.cumsum(lse)]))
+            order.append([np.lexsort((np.arange(V), -z[r, k, j]))[:topk] for j in range(L)])
+            ztop.append([z[r, k, j, order[k][j]] for j in range(L)])
+        tok[r, 0] = int(root_tokens[r])
+        node_of = {(): 0}                          # token sequence -> node
+        seq_sz = {}                                # (mode, rank sequence) -> logit sum of the path
+        keys_seen = []
+
+        def entry(k, sz, ranks):
+            d = len(ranks)
+            return (-((sz - C[k][d]) + lp[r, k]), d, ranks, k, sz)
+
+        heap = []
+        if n_nodes > 1:
+            for k in range(M):
+                heapq.heappush(heap, entry(k, ztop[k][0][0], (0,)))
+        n = 1
+        while heap and n < n_nodes:
+            negs, d, ranks, k, sz = heapq.heappop(heap)
+            keys_seen.append((-negs, sz, C[k][d], lp[r, k]))
+            seq_sz[(k, ranks)] = sz
+            seq = tuple(int(order[k][j][ranks[j]]) for j in range(d))
+            if seq not in node_of:
+                node_of[seq] = n
+                par[r, n] = node_of[seq[:-1]]
+                tok[r, n] = seq[-1]
+                sc[r, n] = -negs
+                n += 1
+            rk = ranks[-1]
+            if rk + 1 < topk:                      # next sibling under mode k
+                psz = seq_sz[(k, ranks[:-1])] if d > 1 else 0.0
+                heapq.heappush(heap, entry(k, psz + ztop[k][d - 1][rk + 1], ranks[:-1] + (rk + 1,)))
+            if d < L:                              # first child under mode k
+                heapq.heappush(heap, entry(k, sz + ztop[k][d][0], ranks + (0,)))
+        if n < n_nodes:                            # fewer distinct prefixes than nodes
+            tok[r, n:] = -1
+            sc[r, n:] = np.nan
+        keys_seen += [(-e[0], e[4], C[e[3]][e[1]], lp[r, e[3]]) for e in heap]
+        keys_seen.sort()
+        for (s1, z1, c1, p1), (s2, z2, c2, p2) in zip(keys_seen, keys_seen[1:]):
+            if s2 - s1 <= tie_eps and not (z1 == z2 and c1 == c2 and p1 == p2):
                 near[r] = True
                 break
     return BuiltTree(par, tok, sc, near)

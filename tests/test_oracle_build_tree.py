@@ -12,7 +12,11 @@ What fixes the oracle here, other than its own heap:
   * node scores are logs of products of library softmax probabilities;
   * equal logits everywhere: every prefix of one depth ties, so the order is
     by depth, then lexicographic rank (closed form);
-  * top-1: the chain of per-position argmaxes.
+  * top-1: the chain of per-position argmaxes;
+  * the merged heap over several modes ("Multi-Future Drafting" Prop. 6)
+    returns the B - 1 distinct prefixes with the largest best-mode score, by
+    brute force over the union of the modes' universes; one mode is the
+    single-mode builder; identical modes collapse to it.
 """
 import heapq
 import itertools
@@ -156,3 +160,81 @@ def test_bf16_input_and_universe_limit():
     np.testing.assert_array_equal(a.tokens, b.tokens)
     with pytest.raises(oracle.OracleError):
         oracle.build_tree(z, "f32", 2, 8, np.array([0]))   # 2 + 4 = 6 < 7 prefixes
+
+
+# ----------------------------------------------------------------------------
+# The merged heap over several modes ("Multi-Future Drafting", App. B, Prop. 6)
+def _brute_force_modes(z, K, B, lp):
+    """Every prefix that some mode's retained universe holds, scored by the
+    best such mode's log pi_k + log q_k(v) (scipy log-softmax), the B - 1
+    largest, best first (ties: shorter first)."""
+    M, L, V = z.shape
+    logq = scipy.special.log_softmax(z.astype(np.float64), axis=-1)
+    keep = [[_retained(z[k, j], K) for j in range(L)] for k in range(M)]
+    best = {}
+    for k in range(M):
+        for d in range(1, L + 1):
+            for ranks in itertools.product(range(K), repeat=d):
+                seq = tuple(int(keep[k][j][ranks[j]]) for j in range(d))
+                s = lp[k] + sum(logq[k, j, seq[j]] for j in range(d))
+                if seq not in best or s > best[seq]:
+                    best[seq] = s
+    chosen = sorted(best.items(), key=lambda kv: (-kv[1], len(kv[0])))[:B - 1]
+    return chosen
+
+
+@pytest.mark.parametrize("seed,M,L,V,K,B,prior", [(0, 3, 3, 9, 3, 25, False), (1, 4, 2, 12, 4, 20, True),
+                                                  (2, 2, 4, 6, 2, 30, True), (3, 8, 2, 40, 6, 33, False)])
+def test_merged_heap_is_top_distinct_prefixes(seed, M, L, V, K, B, prior):
+    """Prop. 6: the B - 1 distinct prefixes with the largest best-mode score,
+    in nonincreasing order; node scores are those best-mode scores."""
+    rng = np.random.default_rng(seed)
+    z = (rng.standard_normal((1, M, L, V)) * 2.0).astype(np.float32)
+    # modes share some structure: mode 1 copies mode 0's first position
+    if M > 1:
+        z[0, 1, 0] = z[0, 0, 0]
+    lp = np.log(rng.dirichlet(np.ones(M))).astype(np.float32) if prior else None
+    got = oracle.build_tree_modes(z, "f32", K, B, np.array([0]), log_prior=None if lp is None else lp[None])
+    assert not got.near_tie[0]
+    want = _brute_force_modes(z[0], K, B, np.full(M, -np.log(M)) if lp is None else lp.astype(np.float64))
+    seqs = [()]
+    for n in range(1, B):
+        seqs.append(seqs[got.parents[0, n]] + (int(got.tokens[0, n]),))
+    assert [s for s, _ in want] == seqs[1:]
+    np.testing.assert_allclose(got.scores[0, 1:], [v for _, v in want], rtol=0, atol=1e-11)
+    # distinct siblings, parents before children
+    for n in range(1, B):
+        assert 0 <= got.parents[0, n] < n
+    assert len(set(seqs)) == B
+
+
+def test_one_mode_is_the_single_mode_builder():
+    z = (np.random.default_rng(21).standard_normal((3, 1, 6, 500)) * 3).astype(np.float32)
+    a = oracle.build_tree(z[:, 0], "f32", 16, 80, np.arange(3))
+    b = oracle.build_tree_modes(z, "f32", 16, 80, np.arange(3))
+    np.testing.assert_array_equal(a.parents, b.parents)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    np.testing.assert_array_equal(a.scores, b.scores)
+
+
+def test_identical_modes_collapse():
+    """Copies of one mode under a uniform prior give the one-mode tree (every
+    prefix ties across the copies; the lowest mode creates the node), with
+    scores shifted by log(1 / M)."""
+    z1 = (np.random.default_rng(22).standard_normal((1, 1, 4, 200)) * 3).astype(np.float32)
+    z = np.repeat(z1, 4, axis=1)
+    a = oracle.build_tree(z1[:, 0], "f32", 8, 50, np.array([0]))
+    b = oracle.build_tree_modes(z, "f32", 8, 50, np.array([0]))
+    np.testing.assert_array_equal(a.parents, b.parents)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    np.testing.assert_allclose(b.scores[0, 1:], a.scores[0, 1:] - np.log(4), rtol=0, atol=1e-12)
+
+
+def test_merged_heap_short_universe():
+    """Two identical modes of 2 + 4 prefixes each hold 6 distinct prefixes: a
+    tree of 13 nodes keeps its last 6 unfilled."""
+    z = (np.random.default_rng(23).standard_normal((1, 1, 2, 30)) * 2).astype(np.float32)
+    got = oracle.build_tree_modes(np.repeat(z, 2, axis=1), "f32", 2, 13, np.array([0]))
+    assert np.all(got.parents[0, 1:7] >= 0)
+    assert np.all(got.parents[0, 7:] == -1) and np.all(got.tokens[0, 7:] == -1)
+    assert np.all(np.isnan(got.scores[0, 7:]))
