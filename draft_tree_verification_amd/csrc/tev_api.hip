@@ -33,6 +33,23 @@ float log2e_scale(float inv_temperature) {
     return (float)((double)inv_temperature * 1.4426950408889634);
 }
 
+bool tree_shape_ok(int R, int M, int L, int V, int K) {
+    if (R < 1 || M < 1 || M > TB_MAX_MODES || L < 1 || L > TB_MAX_L || V < 1 || K < 1 || K > TB_MAX_K ||
+        K > V)
+        return false;
+    const long long ns = tb_slabs(V);
+    return ns <= TB_MAX_SLABS && ns * K <= 8192 && (long long)R * M * L <= 65535;
+}
+// K + K^2 + ... + K^L, capped once it reaches `cap`
+long long universe_size(int K, int L, long long cap) {
+    long long u = 0, pw = 1;
+    for (int d = 1; d <= L && u < cap; d++) {
+        pw *= K;
+        u += pw;
+    }
+    return u;
+}
+
 tev_status hip_status(hipError_t e) { return e == hipSuccess ? TEV_OK : TEV_ERR_HIP; }
 
 }  // namespace
@@ -150,11 +167,10 @@ tev_status tev_exit_loss(const void *draft_logits, int dtype, const int32_t *par
                                        (hipStream_t)stream));
 }
 
+
 size_t tev_build_tree_workspace_bytes(int R, int L, int V, int K) {
-    if (R < 1 || L < 1 || L > TB_MAX_L || V < 1 || K < 1 || K > TB_MAX_K || K > V) return 0;
-    const long long ns = tb_slabs(V);
-    if (ns > TB_MAX_SLABS || ns * K > 8192 || (long long)R * L > 65535) return 0;
-    return tree_ws_layout(R, L, V, K).total;
+    if (!tree_shape_ok(R, 1, L, V, K)) return 0;
+    return tree_modes_ws_layout(R, 1, L, V, K, 0).total;
 }
 
 tev_status tev_build_tree(const void *draft_logits, int dtype, const int32_t *root_tokens, int R,
@@ -164,17 +180,33 @@ tev_status tev_build_tree(const void *draft_logits, int dtype, const int32_t *ro
     if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
     const size_t need = tev_build_tree_workspace_bytes(R, L, V, K);
     if (need == 0 || B < 1 || B > TEV_MAX_NODES) return TEV_ERR_SHAPE;
-    // the retained universe must hold B - 1 prefixes: K + K^2 + ... + K^L
-    long long universe = 0, pw = 1;
-    for (int d = 1; d <= L && universe < B; d++) {
-        pw *= K;
-        universe += pw;
-    }
-    if (universe < B - 1) return TEV_ERR_SHAPE;
+    if (universe_size(K, L, B) < B - 1) return TEV_ERR_SHAPE;   // the universe must hold B - 1 prefixes
     if (workspace_bytes < need) return TEV_ERR_WORKSPACE;
-    return hip_status(launch_build_tree(draft_logits, dtype, vec_ok(draft_logits, dtype, V), root_tokens,
-                                        R, L, V, K, B, parents, tokens, scores, (char *)workspace,
-                                        (hipStream_t)stream));
+    return hip_status(launch_build_tree(draft_logits, dtype, vec_ok(draft_logits, dtype, V), nullptr, 0.0,
+                                        root_tokens, R, 1, L, V, K, B, parents, tokens, scores,
+                                        (char *)workspace, (hipStream_t)stream));
+}
+
+size_t tev_build_tree_modes_workspace_bytes(int R, int M, int L, int V, int K, int B) {
+    if (!tree_shape_ok(R, M, L, V, K) || B < 1 || B > TEV_MAX_NODES) return 0;
+    return tree_modes_ws_layout(R, M, L, V, K, B).total;
+}
+
+tev_status tev_build_tree_modes(const void *draft_logits, int dtype, const float *log_prior,
+                                const int32_t *root_tokens, int R, int M, int L, int V, int K, int B,
+                                int32_t *parents, int32_t *tokens, double *scores, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (!draft_logits || !parents || !tokens || !scores || !workspace) return TEV_ERR_NULL;
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    const size_t need = tev_build_tree_modes_workspace_bytes(R, M, L, V, K, B);
+    if (need == 0) return TEV_ERR_SHAPE;
+    if ((long long)M * universe_size(K, L, B) < B - 1) return TEV_ERR_SHAPE;
+    if (workspace_bytes < need) return TEV_ERR_WORKSPACE;
+    // uniform prior: log(1 / M), the same double the host library computes
+    const double lp_default = M == 1 ? 0.0 : -log((double)M);
+    return hip_status(launch_build_tree(draft_logits, dtype, vec_ok(draft_logits, dtype, V), log_prior,
+                                        lp_default, root_tokens, R, M, L, V, K, B, parents, tokens, scores,
+                                        (char *)workspace, (hipStream_t)stream));
 }
 
 size_t tev_tree_attn_workspace_bytes(int R, int B, int Hq, int Hkv, int D, int P) {

@@ -12,6 +12,7 @@ constexpr int TB_SLAB = TB_THREADS * TB_EPT;       // 8192 logits
 constexpr int TB_MAX_L = 16;                       // draft positions
 constexpr int TB_MAX_K = 128;                      // retained tokens per position
 constexpr int TB_MAX_SLABS = 64;                   // one slab list per lane in the row merge
+constexpr int TB_MAX_MODES = 8;                    // draft modes of the merged heap
 
 inline int tb_slabs(int V) { return (V + TB_SLAB - 1) / TB_SLAB; }
 
@@ -45,8 +46,35 @@ inline TreeWs tree_ws_layout(int R, int L, int V, int K) {
     return W;
 }
 
-hipError_t launch_build_tree(const void *draft_logits, int dtype, bool vec, const int32_t *root_tokens,
-                             int R, int L, int V, int K, int B, int32_t *parents, int32_t *tokens,
-                             double *scores, char *ws, hipStream_t st);
+// Several draft modes: the per-mode part above for R * M (request, mode)
+// pairs, then the modes' emitted streams.  The request flag words come first
+// (the per-mode part keeps its own per-mode ones).
+//   status    u32 [R]
+//   base      TreeWs of R * M requests
+//   stream    40-byte records [R * M][B]: key, rank sequence, parent, token, depth
+//   stream_n  i32 [R * M]    nodes each mode emitted (root included)
+struct TreeModesWs {
+    size_t status, base_off, stream, stream_n, total;
+    TreeWs base;
+};
+
+inline TreeModesWs tree_modes_ws_layout(int R, int M, int L, int V, int K, int B) {
+    TreeModesWs W{};
+    size_t o = 0;
+    W.status = o;   o = align_up(o + 4 * (size_t)R, 256);
+    W.base_off = o;
+    W.base = tree_ws_layout(R * M, L, V, K);
+    o = align_up(o + W.base.total, 256);
+    W.stream = o;   o = align_up(o + 40 * (size_t)R * M * B, 256);
+    W.stream_n = o; o = align_up(o + 4 * (size_t)R * M, 256);
+    W.total = o;
+    return W;
+}
+
+// M = 1: the single-mode search writes the tree; M > 1: per-mode streams and
+// the merge.  log_prior [R][M] or NULL (then every key adds lp_default).
+hipError_t launch_build_tree(const void *draft_logits, int dtype, bool vec, const float *log_prior,
+                             double lp_default, const int32_t *root_tokens, int R, int M, int L, int V, int K,
+                             int B, int32_t *parents, int32_t *tokens, double *scores, char *ws, hipStream_t st);
 
 }  // namespace tev

@@ -248,6 +248,13 @@ __device__ __forceinline__ void set_rank(uint64_t &hi, uint64_t &lo, int d, int 
     }
 }
 
+// One emitted node of a mode's search, kept for the merge across modes.
+struct StreamRec {
+    double key;
+    uint64_t hi, lo;        // rank sequence under the mode
+    int parent, token, depth, pad;
+};
+
 // Frontier slots.  Slot p (lane p mod 64, register p / 64) belongs to node
 // p and holds the next not yet emitted child of p: first its rank-0 child,
 // then, each time that child is popped, the next sibling.  So a pop changes
@@ -280,15 +287,20 @@ template <int SLOTS>
 __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top, const double *__restrict__ lse,
                                                 const unsigned *__restrict__ row_flag,
                                                 const int32_t *__restrict__ root_tokens, int L, int K, int B,
+                                                const float *__restrict__ log_prior, double lp_default,
                                                 unsigned *__restrict__ status, int32_t *__restrict__ parents,
-                                                int32_t *__restrict__ tokens, double *__restrict__ scores) {
+                                                int32_t *__restrict__ tokens, double *__restrict__ scores,
+                                                StreamRec *__restrict__ stream, int32_t *__restrict__ stream_n) {
     constexpr int NLD = TB_MAX_L * TB_MAX_K / 64;     // top-K entries per lane
     __shared__ float s_tz[TB_MAX_L * TB_MAX_K];
     __shared__ int s_tt[TB_MAX_L * TB_MAX_K];
     __shared__ int s_par[TEV_MAX_NODES], s_idx[TEV_MAX_NODES];
     __shared__ double s_sc[TEV_MAX_NODES];
+    __shared__ uint64_t s_hi[TEV_MAX_NODES], s_lo[TEV_MAX_NODES];
     const int lane = threadIdx.x, r = blockIdx.x;
     const float qnan = __builtin_nanf("");
+    // the mode's log prior: every key is (logit sum - logsumexp sum) + lp
+    const double lp = log_prior ? (double)log_prior[r] : lp_default;
     // every load first, then the LDS stores
     const int LK = L * K;
     uint64_t kv[NLD];
@@ -320,6 +332,10 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
     const float zr1 = (lane >= 1 && lane <= L && K > 1) ? s_tz[(lane - 1) * K + 1] : qnan;
     if (lane == 0) status[r] = fl;
     if (fl) {
+        if (stream) {
+            if (lane == 0) stream_n[r] = 0;
+            return;
+        }
         for (int n = lane; n < B; n += 64) {
             parents[(size_t)r * B + n] = -1;
             tokens[(size_t)r * B + n] = -1;
@@ -334,7 +350,7 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
         const double sz = (double)wave::readlane_f(zr0, 1);
         if (lane == 0) {
             f[0].sz = sz;
-            f[0].s = sz - wave::readlane_d(creg, 1);
+            f[0].s = (sz - wave::readlane_d(creg, 1)) + lp;
             f[0].zn = wave::readlane_f(zr1, 1);
             f[0].depth = 1;
         }
@@ -388,6 +404,8 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
             s_par[n] = parent;
             s_idx[n] = (d - 1) * K + rk;
             s_sc[n] = ws;
+            s_hi[n] = whi;
+            s_lo[n] = wlo;
         }
         // the winner's slot moves on to the next sibling (or empties)
         if (lane == wl) {
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
             if (rk + 1 < K) {
                 sib.psz = mine.psz;
                 sib.sz = mine.psz + (double)mine.zn;
-                sib.s = sib.sz - wave::readlane_d(creg, d);
+                sib.s = (sib.sz - wave::readlane_d(creg, d)) + lp;
                 sib.hi = whi;
                 sib.lo = wlo;
                 set_rank(sib.hi, sib.lo, d, rk + 1);
@@ -411,7 +429,7 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
             Slot ch;
             ch.psz = wsz;
             ch.sz = wsz + (double)wave::readlane_f(zr0, d + 1);
-            ch.s = ch.sz - wave::readlane_d(creg, d + 1);
+            ch.s = (ch.sz - wave::readlane_d(creg, d + 1)) + lp;
             ch.hi = whi;                                  // rank 0 at depth d + 1: byte already 0
             ch.lo = wlo;
             ch.zn = wave::readlane_f(zr1, d + 1);
@@ -422,6 +440,22 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
         }
     }
     __syncthreads();
+    if (stream) {
+        // the mode's pop order, for the merge across modes
+        for (int i = 1 + lane; i < n; i += 64) {
+            StreamRec e;
+            e.key = s_sc[i];
+            e.hi = s_hi[i];
+            e.lo = s_lo[i];
+            e.parent = s_par[i];
+            e.token = s_tt[s_idx[i]];
+            e.depth = s_idx[i] / K + 1;
+            e.pad = 0;
+            stream[(size_t)r * B + i] = e;
+        }
+        if (lane == 0) stream_n[r] = n;
+        return;
+    }
     for (int i = lane; i < B; i += 64) {
         const bool ok = i == 0 || i < n;
         parents[(size_t)r * B + i] = i == 0 ? -1 : (ok ? s_par[i] : -1);
@@ -430,46 +464,174 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
     }
 }
 
-template <typename T, bool VEC>
-hipError_t launch_typed(const void *z, const int32_t *root_tokens, int R, int L, int V, int K, int B,
-                        int32_t *parents, int32_t *tokens, double *scores, char *ws, hipStream_t st) {
-    const TreeWs W = tree_ws_layout(R, L, V, K);
-    const int ns = tb_slabs(V);
-    unsigned *flag = (unsigned *)(ws + W.flag);
-    float *slab_m = (float *)(ws + W.slab_m);
-    double *slab_s = (double *)(ws + W.slab_s);
-    uint64_t *cand = (uint64_t *)(ws + W.cand);
-    uint64_t *top = (uint64_t *)(ws + W.top);
-    double *lse = (double *)(ws + W.lse);
-    unsigned *row_flag = (unsigned *)(ws + W.row_flag);
-    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(R * L)), TB_THREADS, ((size_t)TB_EPT * K + 16) * 8, st>>>(
-        static_cast<const T *>(z), V, ns, K, flag, slab_m, slab_s, cand);
-    k_tb_rows<<<R * L, TB_THREADS, ((size_t)(8192 / TB_THREADS) * K + 16) * 8, st>>>(flag, slab_m, slab_s, cand, ns, K,
-                                                                            top, lse, row_flag);
-    unsigned *status = (unsigned *)(ws + W.status);
-    switch ((B + 63) / 64) {
-    case 1: k_tb_heap<1><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
-    case 2: k_tb_heap<2><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
-    case 3: k_tb_heap<3><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
-    default: k_tb_heap<4><<<R, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, status, parents, tokens, scores); break;
+// The merge across draft modes ("Multi-Future Drafting", App. B and Prop. 6):
+// every mode's emitted nodes, each mode in its own pop order, are taken in the
+// order in which the merged heap pops them (key, then depth, rank sequence,
+// mode).  The first entry of each distinct prefix creates a node (the prefix
+// is its parent's node and its token, looked up in an LDS hash table); a later
+// entry of the same prefix only maps its mode-local index to that node.  A
+// mode-local parent always precedes its children in the mode's order, so its
+// node is known.  One wave per request; lane k holds mode k's next entry.
+constexpr int TB_HASH = 1024;                    // >= 4 B slots: short probe chains
+
+__global__ __launch_bounds__(64) void k_tb_merge(const StreamRec *__restrict__ stream,
+                                                 const int32_t *__restrict__ stream_n,
+                                                 const unsigned *__restrict__ mode_status,
+                                                 const int32_t *__restrict__ root_tokens, int M, int B,
+                                                 unsigned *__restrict__ status, int32_t *__restrict__ parents,
+                                                 int32_t *__restrict__ tokens, double *__restrict__ scores) {
+    extern __shared__ StreamRec s_st[];              // M * B records
+    __shared__ int16_t s_map[TB_MAX_MODES * TEV_MAX_NODES];
+    __shared__ uint64_t s_hkey[TB_HASH];
+    __shared__ int s_hval[TB_HASH];
+    __shared__ int s_par[TEV_MAX_NODES], s_tok[TEV_MAX_NODES];
+    __shared__ double s_sc[TEV_MAX_NODES];
+    const int lane = threadIdx.x, r = blockIdx.x;
+    unsigned fl = 0u;
+    int len = 0;
+    if (lane < M) {
+        fl = mode_status[(size_t)r * M + lane];
+        len = stream_n[(size_t)r * M + lane];
     }
+    fl = __ballot(fl != 0u) != 0ull ? (unsigned)TEV_FLAG_NONFINITE : 0u;
+    if (lane == 0) status[r] = fl;
+    if (fl) {
+        for (int i = lane; i < B; i += 64) {
+            parents[(size_t)r * B + i] = -1;
+            tokens[(size_t)r * B + i] = -1;
+            scores[(size_t)r * B + i] = __builtin_nan("");
+        }
+        return;
+    }
+    for (int i = lane; i < M * B; i += 64) {
+        s_st[i] = stream[(size_t)r * M * B + i];       // entry 0 of a mode (the root) is not read
+        s_map[i] = (int16_t)((i % B) == 0 ? 0 : -1);   // every mode's root is node 0
+    }
+    for (int i = lane; i < TB_HASH; i += 64) s_hkey[i] = 0ull;
+    __syncthreads();
+    int idx = 1, n = 1;
+    while (n < B) {
+        const bool valid = lane < M && idx < len;
+        StreamRec e{0.0, 0ull, 0ull, 0, 0, 0, 0};
+        if (valid) e = s_st[lane * B + idx];
+        const float k32 = valid ? (float)e.key : -kInf;
+        const float m32 = wave::max_f32(k32);
+        uint64_t ball = __ballot(valid && k32 == m32);
+        if (ball == 0ull) break;                        // every stream is used up
+        int wl = __ffsll((long long)ball) - 1;
+        ball &= ball - 1;
+        if (ball) {                                     // key, depth, rank sequence, mode
+            double bk = wave::readlane_d(e.key, wl);
+            int bd = __builtin_amdgcn_readlane(e.depth, wl);
+            uint64_t bh = readlane_u64(e.hi, wl), bl = readlane_u64(e.lo, wl);
+            while (ball) {
+                const int l = __ffsll((long long)ball) - 1;
+                ball &= ball - 1;
+                const double k2 = wave::readlane_d(e.key, l);
+                const int d2 = __builtin_amdgcn_readlane(e.depth, l);
+                const uint64_t h2 = readlane_u64(e.hi, l), l2 = readlane_u64(e.lo, l);
+                const bool b = k2 != bk ? k2 > bk : d2 != bd ? d2 < bd : h2 != bh ? h2 < bh : l2 < bl;
+                if (b) {
+                    bk = k2; bd = d2; bh = h2; bl = l2;
+                    wl = l;
+                }
+            }
+        }
+        const double key = wave::readlane_d(e.key, wl);
+        const int lpar = __builtin_amdgcn_readlane(e.parent, wl);
+        const int tok = __builtin_amdgcn_readlane(e.token, wl);
+        const int widx = __builtin_amdgcn_readlane(idx, wl);
+        const int P = s_map[wl * B + lpar];
+        // (parent node, token) -> node: linear probing
+        const uint64_t hk = (((uint64_t)(uint32_t)P << 32) | (uint32_t)tok) + 1ull;
+        int h = (int)((hk * 0x9E3779B97F4A7C15ull) >> 54);    // top 10 bits: TB_HASH = 1024
+        int found = -1;
+        for (;;) {
+            const uint64_t kk = s_hkey[h];
+            if (kk == 0ull) break;
+            if (kk == hk) {
+                found = s_hval[h];
+                break;
+            }
+            h = (h + 1) & (TB_HASH - 1);
+        }
+        int node = found;
+        if (found < 0) {
+            node = n;
+            if (lane == 0) {
+                s_hkey[h] = hk;
+                s_hval[h] = n;
+                s_par[n] = P;
+                s_tok[n] = tok;
+                s_sc[n] = key;
+            }
+            n++;
+        }
+        if (lane == 0) s_map[wl * B + widx] = (int16_t)node;
+        if (lane == wl) idx++;
+    }
+    __syncthreads();
+    for (int i = lane; i < B; i += 64) {
+        const bool ok = i < n;
+        parents[(size_t)r * B + i] = (i == 0 || !ok) ? -1 : s_par[i];
+        tokens[(size_t)r * B + i] = i == 0 ? (root_tokens ? root_tokens[r] : 0) : (ok ? s_tok[i] : -1);
+        scores[(size_t)r * B + i] = i == 0 ? 0.0 : (ok ? s_sc[i] : __builtin_nan(""));
+    }
+}
+
+template <typename T, bool VEC>
+hipError_t launch_typed(const void *z, const float *log_prior, double lp_default, const int32_t *root_tokens,
+                        int R, int M, int L, int V, int K, int B, int32_t *parents, int32_t *tokens,
+                        double *scores, char *ws, hipStream_t st) {
+    // M draft modes: the slab, row and search passes treat each (request,
+    // mode) as a request of its own; with M > 1 their searches emit streams
+    // that the merge combines.
+    const TreeModesWs MW = tree_modes_ws_layout(R, M, L, V, K, B);
+    const TreeWs W = MW.base;
+    char *b = ws + MW.base_off;
+    const int G = R * M;
+    const int ns = tb_slabs(V);
+    unsigned *flag = (unsigned *)(b + W.flag);
+    float *slab_m = (float *)(b + W.slab_m);
+    double *slab_s = (double *)(b + W.slab_s);
+    uint64_t *cand = (uint64_t *)(b + W.cand);
+    uint64_t *top = (uint64_t *)(b + W.top);
+    double *lse = (double *)(b + W.lse);
+    unsigned *row_flag = (unsigned *)(b + W.row_flag);
+    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(G * L)), TB_THREADS, ((size_t)TB_EPT * K + 16) * 8, st>>>(
+        static_cast<const T *>(z), V, ns, K, flag, slab_m, slab_s, cand);
+    k_tb_rows<<<G * L, TB_THREADS, ((size_t)(8192 / TB_THREADS) * K + 16) * 8, st>>>(flag, slab_m, slab_s, cand, ns, K,
+                                                                                  top, lse, row_flag);
+    unsigned *hstatus = M == 1 ? (unsigned *)(ws + MW.status) : (unsigned *)(b + W.status);
+    StreamRec *strm = M == 1 ? nullptr : (StreamRec *)(ws + MW.stream);
+    int32_t *strm_n = M == 1 ? nullptr : (int32_t *)(ws + MW.stream_n);
+#define TB_HEAP(SL)                                                                                      \
+    k_tb_heap<SL><<<G, 64, 0, st>>>(top, lse, row_flag, root_tokens, L, K, B, log_prior, lp_default, hstatus, \
+                                    parents, tokens, scores, strm, strm_n)
+    switch ((B + 63) / 64) {
+    case 1: TB_HEAP(1); break;
+    case 2: TB_HEAP(2); break;
+    case 3: TB_HEAP(3); break;
+    default: TB_HEAP(4); break;
+    }
+#undef TB_HEAP
+    if (M > 1)
+        k_tb_merge<<<R, 64, (size_t)M * B * sizeof(StreamRec), st>>>(strm, strm_n, hstatus, root_tokens, M, B,
+                                                                      (unsigned *)(ws + MW.status), parents,
+                                                                      tokens, scores);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_build_tree(const void *draft_logits, int dtype, bool vec, const int32_t *root_tokens,
-                             int R, int L, int V, int K, int B, int32_t *parents, int32_t *tokens,
-                             double *scores, char *ws, hipStream_t st) {
+hipError_t launch_build_tree(const void *draft_logits, int dtype, bool vec, const float *log_prior,
+                             double lp_default, const int32_t *root_tokens, int R, int M, int L, int V, int K,
+                             int B, int32_t *parents, int32_t *tokens, double *scores, char *ws, hipStream_t st) {
+#define TB_ARGS draft_logits, log_prior, lp_default, root_tokens, R, M, L, V, K, B, parents, tokens, scores, ws, st
     if (dtype == TEV_BF16)
-        return vec ? launch_typed<uint16_t, true>(draft_logits, root_tokens, R, L, V, K, B, parents, tokens,
-                                                  scores, ws, st)
-                   : launch_typed<uint16_t, false>(draft_logits, root_tokens, R, L, V, K, B, parents, tokens,
-                                                   scores, ws, st);
-    return vec ? launch_typed<float, true>(draft_logits, root_tokens, R, L, V, K, B, parents, tokens, scores,
-                                           ws, st)
-               : launch_typed<float, false>(draft_logits, root_tokens, R, L, V, K, B, parents, tokens, scores,
-                                            ws, st);
+        return vec ? launch_typed<uint16_t, true>(TB_ARGS) : launch_typed<uint16_t, false>(TB_ARGS);
+    return vec ? launch_typed<float, true>(TB_ARGS) : launch_typed<float, false>(TB_ARGS);
+#undef TB_ARGS
 }
 
 }  // namespace tev

@@ -33,7 +33,7 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
             "tev_verify_round_timed", "tev_predraw", "tev_commit_kv",
             "tev_exit_loss_workspace_bytes", "tev_exit_loss", "tev_build_tree_workspace_bytes",
-            "tev_build_tree"]
+            "tev_build_tree", "tev_build_tree_modes_workspace_bytes", "tev_build_tree_modes"]
 
 
 class TevError(RuntimeError):
@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.tev_build_tree_workspace_bytes.argtypes = [i, i, i, i]
         L.tev_build_tree_workspace_bytes.restype = sz
         L.tev_build_tree.argtypes = [vp, i, vp, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
+        L.tev_build_tree_modes_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.tev_build_tree_modes_workspace_bytes.restype = sz
+        L.tev_build_tree_modes.argtypes = [vp, i, vp, vp, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp]
         L.tev_tree_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.tev_tree_attn_workspace_bytes.restype = sz
         L.tev_tree_attn.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, f, vp, vp, sz, vp]
@@ -80,6 +83,7 @@ def lib() -> ctypes.CDLL:
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
         for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_exit_loss", "tev_build_tree",
+                   "tev_build_tree_modes",
                    "tev_tree_attn", "tev_validate_tree_host",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
@@ -302,6 +306,35 @@ def tev_build_tree(draft_logits: torch.Tensor, K: int, B: int, root_tokens: torc
                               _p(out.parents), _p(out.tokens), _p(out.scores), _p(out.workspace),
                               out.workspace.numel(), _stream())
     _check("tev_build_tree", st)
+    return out
+
+
+def tev_build_tree_modes_workspace_bytes(R: int, M: int, L: int, V: int, K: int, B: int) -> int:
+    return int(lib().tev_build_tree_modes_workspace_bytes(R, M, L, V, K, B))
+
+
+def tev_build_tree_modes(draft_logits: torch.Tensor, K: int, B: int, log_prior: torch.Tensor | None = None,
+                         root_tokens: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         out: BuiltTree | None = None) -> BuiltTree:
+    """Merged heap over M draft modes: draft_logits [R][M][L][V] (bf16 or
+    f32), log_prior float32 [R][M] or None (uniform)."""
+    _need_cuda(draft_logits)
+    for t in (log_prior, root_tokens):
+        if t is not None:
+            _need_cuda(t)
+    R, M, L, V = draft_logits.shape
+    dev = draft_logits.device
+    if out is None:
+        if workspace is None:
+            workspace = torch.empty(max(tev_build_tree_modes_workspace_bytes(R, M, L, V, K, B), 1),
+                                    dtype=torch.uint8, device=dev)
+        out = BuiltTree(torch.empty((R, B), dtype=torch.int32, device=dev),
+                        torch.empty((R, B), dtype=torch.int32, device=dev),
+                        torch.empty((R, B), dtype=torch.float64, device=dev), workspace)
+    st = lib().tev_build_tree_modes(_p(draft_logits), _dtype_code(draft_logits), _p(log_prior), _p(root_tokens),
+                                    R, M, L, V, K, B, _p(out.parents), _p(out.tokens), _p(out.scores),
+                                    _p(out.workspace), out.workspace.numel(), _stream())
+    _check("tev_build_tree_modes", st)
     return out
 
 

@@ -333,7 +333,9 @@ def _request_wide_zipf(cfg, r, B=128, L=16, V=V_QWEN):
     return parents, tokens, f32_to_bf16_bits(logits)
 
 
-def _request_mixture(cfg, r, B=256, L=16, V=V_QWEN, K=8):
+def _mixture_ells(cfg, r, L=16, V=V_QWEN, K=8):
+    """The K modes' position-wise draft logits of a mixture request and its
+    two futures A, B."""
     mrng = _rng(cfg, r, S_MODES)
     A = mrng.choice(V, size=L + 1, replace=False)
     Bf = np.empty(L + 1, np.int64)
@@ -346,12 +348,18 @@ def _request_mixture(cfg, r, B=256, L=16, V=V_QWEN, K=8):
     futures = [A, A, A, Bf, Bf, Bf,
                mrng.integers(0, V, size=L + 1), mrng.integers(0, V, size=L + 1)]
     drng = _rng(cfg, r, S_DRAFT)
-    qs = np.empty((K, L, V))
+    ells = np.empty((K, L, V))
     for k in range(K):
         ell = _peaked_draft(drng, L, V)
         for j in range(L):
             ell[j, futures[k][j]] = ell[j].max() + 2.0
-        qs[k] = _softmax64(ell)
+        ells[k] = ell
+    return ells, A, Bf
+
+
+def _request_mixture(cfg, r, B=256, L=16, V=V_QWEN, K=8):
+    ells, A, Bf = _mixture_ells(cfg, r, L, V, K)
+    qs = np.stack([_softmax64(ells[k]) for k in range(K)])
     parents, tokens = merged_heap_tree(qs, B)
     tokens[0] = _rng(cfg, r, S_ROOT).integers(0, V)
     # target: bimodal masses -> log -> bf16
@@ -457,9 +465,19 @@ def draft_rows(name: str, requests: int | None = None) -> np.ndarray:
         elif name == "qwen3_8b_wide":
             rows.append(_wide_ell(cfg, r)[:16])
         else:
-            raise KeyError(f"{name} has no single position-wise drafter")
+            raise KeyError(f"{name} has no single position-wise drafter (see draft_rows_modes)")
     z = np.stack(rows).astype(np.float32)
     return z if dtype == "f32" else f32_to_bf16_bits(z)
+
+
+def draft_rows_modes(name: str = "mixture") -> np.ndarray:
+    """The K draft modes' position-wise logits of the mixture workload:
+    [R][K][L][V] bf16 bits (mode k, row j scores depth j + 1)."""
+    if name != "mixture":
+        raise KeyError(name)
+    cfg, R, *_ = CONFIGS[name]
+    z = np.stack([_mixture_ells(cfg, r)[0] for r in range(R)]).astype(np.float32)
+    return f32_to_bf16_bits(z)
 
 
 def make_custom(name: str, *, R: int = 1, B: int = 16, V: int = 1000, dtype: str = "f32",

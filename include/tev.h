@@ -305,6 +305,33 @@ tev_status tev_build_tree(const void *draft_logits, int dtype, const int32_t *ro
                           double *scores, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The merged heap over M draft modes ("Multi-Future Drafting" App. B and
+ * Prop. 6): the tree of the B - 1 distinct prefixes with the largest
+ * best-mode score s(v) = max_k s_k(v), nodes in the order of their first
+ * pops.
+ *
+ * draft_logits [R][M][L][V]: mode k's position-wise logits; mode k keeps its
+ *           own K most likely tokens per position (as tev_build_tree).
+ * log_prior float [R][M] (device) = log pi_k, or NULL for the uniform prior.
+ *   s_k(v) = (sum_j z_{k,j,y_j} - sum_j lse_{k,j}) + log pi_k
+ * The merged heap pops entries (k, v) by key s_k(v) (equal keys: shorter
+ * prefix, then smaller rank sequence, then smaller k); the first pop of each
+ * distinct prefix creates its node, with score s(v).  With M = 1 and no prior
+ * this is tev_build_tree.  If the modes' universes hold fewer than B - 1
+ * distinct prefixes, the missing nodes get parent and token -1 and score NaN.
+ * Outputs, flags and limits as tev_build_tree, with 1 <= M <= 8,
+ * R * M * L <= 65535 and M (K + ... + K^L) >= B - 1; the workspace holds
+ * tev_build_tree_modes_workspace_bytes(R, M, L, V, K, B) bytes (flag words:
+ * tev_read_device_status kind 4).
+ * ------------------------------------------------------------------------ */
+size_t tev_build_tree_modes_workspace_bytes(int R, int M, int L, int V, int K, int B);
+
+tev_status tev_build_tree_modes(const void *draft_logits, int dtype, const float *log_prior,
+                                const int32_t *root_tokens, int R, int M, int L, int V, int K, int B,
+                                int32_t *parents, int32_t *tokens, double *scores, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Host-side helpers.
  * ------------------------------------------------------------------------ */
 

@@ -102,6 +102,16 @@ def test_argument_errors_return_before_any_launch():
     assert L.tev_build_tree(fake, 1, null, 1, 2, 151936, 3, 14, fake, fake, fake, fake, need_t, s) == 2  # 3 + 9 < 13
     assert L.tev_build_tree(fake, 1, null, 1, 16, 151936, 64, 257, fake, fake, fake, fake, need_t, s) == 2
     assert L.tev_build_tree(fake, 1, null, 1, 16, 151936, 64, 64, fake, fake, fake, fake, need_t - 1, s) == 5
+    # merged heap over modes
+    need_m = L.tev_build_tree_modes_workspace_bytes(1, 8, 16, 151936, 128, 256)
+    assert need_m > 0
+    assert L.tev_build_tree_modes_workspace_bytes(1, 9, 16, 151936, 128, 256) == 0   # M > 8
+    assert L.tev_build_tree_modes(fake, 1, null, null, 1, 8, 16, 151936, 128, 256, fake, fake, fake, fake,
+                                  need_m - 1, s) == 5
+    assert L.tev_build_tree_modes(fake, 1, null, null, 1, 2, 1, 151936, 3, 8, fake, fake, fake, fake,
+                                  need_m, s) == 2                                   # 2 x 3 < 7 prefixes
+    assert L.tev_build_tree_modes(null, 1, null, null, 1, 8, 16, 151936, 128, 256, fake, fake, fake, fake,
+                                  need_m, s) == 1
     # exports
     assert L.tev_export_residual_cdf(fake, 1, fake, fake, 1, 4, 10, 1.0, fake, need, 1, 0, fake, s) == 2
     assert L.tev_read_device_status(null, 0, 1, 4, 10, fake, s) == 1

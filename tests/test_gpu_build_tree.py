@@ -151,3 +151,96 @@ def test_repeat_is_bit_identical():
     b = _gpu(z, "bf16", 32, 96, np.zeros(2, np.int32))
     for x, y in zip(a[:3], b[:3]):
         np.testing.assert_array_equal(x, y)
+
+
+# ----------------------------------------------------------------------------
+# Several draft modes: the merged heap ("Multi-Future Drafting", App. B)
+def _gpu_modes(z, dtype, K, B, roots, lp=None):
+    res = tev.tev_build_tree_modes(tev.to_device_logits(z, dtype), K, B,
+                                   None if lp is None else torch.from_numpy(lp).cuda(),
+                                   tev.to_device_i32(roots))
+    torch.cuda.synchronize()
+    return res.parents.cpu().numpy(), res.tokens.cpu().numpy(), res.scores.cpu().numpy(), res
+
+
+def _check_valid_modes(z64, K, B, lp, par, tok, sc, ref_scores):
+    """Distinct prefixes, each scored by its best mode among those whose
+    retained universe holds it; best first; as a set the oracle's scores.
+    Unfilled nodes (fewer distinct prefixes than nodes) come last."""
+    M, L, V = z64.shape
+    lse = np.array([[np.logaddexp.reduce(z64[k, j]) for j in range(L)] for k in range(M)])
+    keep = [[set(np.lexsort((np.arange(V), -z64[k, j]))[:K].tolist()) for j in range(L)] for k in range(M)]
+    n = B
+    while n > 1 and par[n - 1] < 0:
+        n -= 1
+    assert np.all(tok[n:] == -1)
+    seqs = [()]
+    for i in range(1, n):
+        assert 0 <= par[i] < i
+        seq = seqs[par[i]] + (int(tok[i]),)
+        seqs.append(seq)
+        best = -np.inf
+        for k in range(M):
+            if all(seq[j] in keep[k][j] for j in range(len(seq))):
+                best = max(best, sum(z64[k, j, seq[j]] - lse[k, j] for j in range(len(seq))) + lp[k])
+        assert abs(sc[i] - best) <= 1e-8
+    assert len(set(seqs)) == len(seqs)
+    assert np.all(np.diff(sc[1:n]) <= SCORE_ABS)
+    ref = ref_scores[1:][~np.isnan(ref_scores[1:])]
+    np.testing.assert_allclose(np.sort(sc[1:n]), np.sort(ref), rtol=0, atol=1e-8)
+
+
+def _compare_modes(z, dtype, K, B, lp=None, seed=0):
+    R, M = z.shape[:2]
+    roots = np.random.default_rng(seed).integers(0, z.shape[3], size=R).astype(np.int32)
+    par, tok, sc, res = _gpu_modes(z, dtype, K, B, roots, lp)
+    ref = oracle.build_tree_modes(z, dtype, K, B, roots, log_prior=lp, tie_eps=SCORE_ABS)
+    assert not np.any(tev.tev_read_device_status(res.workspace, 4, R))
+    exact = 0
+    for r in range(R):
+        if not ref.near_tie[r]:
+            np.testing.assert_array_equal(par[r], ref.parents[r])
+            np.testing.assert_array_equal(tok[r], ref.tokens[r])
+            np.testing.assert_allclose(sc[r], ref.scores[r], rtol=0, atol=SCORE_ABS)
+            exact += 1
+        else:
+            lpr = (np.full(M, -np.log(M)) if lp is None else lp[r].astype(np.float64))
+            _check_valid_modes(_widen(z[r], dtype), K, B, lpr, par[r], tok[r], sc[r], ref.scores[r])
+    return exact
+
+
+MODE_CASES = [
+    dict(R=2, M=3, L=4, V=1000, K=8, B=60, dtype="f32", prior=False),
+    dict(R=2, M=4, L=5, V=20000, K=32, B=128, dtype="bf16", prior=True),
+    dict(R=1, M=8, L=3, V=5000, K=16, B=256, dtype="f32", prior=True),
+    dict(R=3, M=2, L=2, V=777, K=4, B=30, dtype="f32", prior=False),       # scalar loads, short universes
+]
+
+
+@pytest.mark.parametrize("case", MODE_CASES, ids=lambda c: f"R{c['R']}_M{c['M']}_L{c['L']}_V{c['V']}_K{c['K']}_B{c['B']}")
+def test_merged_heap_matches_oracle(case):
+    GP.log(f"[build_tree_modes] {case}")
+    rng = np.random.default_rng(case["V"] + case["M"])
+    z = (rng.standard_normal((case["R"], case["M"], case["L"], case["V"])) * 3.0).astype(np.float32)
+    z[:, 1] = np.where(rng.uniform(size=z[:, 1].shape) < 0.5, z[:, 0], z[:, 1])   # modes share tokens
+    if case["dtype"] == "bf16":
+        z = W.f32_to_bf16_bits(z)
+    lp = np.log(rng.dirichlet(np.ones(case["M"]), size=case["R"])).astype(np.float32) if case["prior"] else None
+    assert _compare_modes(z, case["dtype"], case["K"], case["B"], lp) >= 1
+
+
+def test_one_mode_equals_single_mode_builder():
+    z = W.f32_to_bf16_bits((np.random.default_rng(31).standard_normal((2, 1, 16, 30000)) * 4).astype(np.float32))
+    roots = np.array([3, 4], np.int32)
+    a = _gpu(z[:, 0].copy(), "bf16", 32, 100, roots)
+    b = _gpu_modes(z, "bf16", 32, 100, roots)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_mixture_workload_modes():
+    """The mixture workload's 8 draft modes (V = 151936 bf16, 16 positions),
+    K = 128 tokens kept per mode and position, B = 256."""
+    z = W.draft_rows_modes("mixture")
+    GP.log(f"[build_tree_modes] mixture M={z.shape[1]} L={z.shape[2]} V={z.shape[3]} K=128 B=256")
+    assert _compare_modes(z, "bf16", 128, 256) >= 1
