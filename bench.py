@@ -508,13 +508,33 @@ def main():
             exit_loss[name] = {"us": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         exit_loss["loss_value"] = float(lo.loss[0])
-        # the best-first tree builder on the same draft rows (B tokens kept per
-        # position, the budget of the workload's own trees)
-        Kb = min(B, 128)
-        tb = tev.tev_build_tree(zring[0], Kb, B, base["tok"][:, 0].contiguous())
+        log(f"[bench] tev_exit_loss over {R * H} draft rows: loss {exit_loss['loss']['us']:.2f} us, "
+            f"loss + grad {exit_loss['loss_and_grad']['us']:.2f} us "
+            f"({exit_loss['loss_and_grad']['achieved_gbs']:.0f} GB/s)")
+        del zring
 
-        def fn_tb(j):
-            tev.tev_build_tree(zring[j % len(zring)], Kb, B, out=tb)
+    # the tree builder on the workload's own draft rows (B tokens kept per
+    # position, up to 128; the mixture's 8 draft modes through the merged heap)
+    try:
+        zb, nmodes = W.draft_rows(wl.name), 1
+    except KeyError:
+        zb, nmodes = (W.draft_rows_modes(wl.name), 8) if wl.name == "mixture" else (None, 0)
+    if zb is not None:
+        zb0 = to_dev(zb)
+        zbring = [zb0] + [zb0.clone() for _ in range(max(1, min(64, int(np.ceil(
+            args.ring_bytes / (zb0.numel() * zb0.element_size()))))) - 1)]
+        Kb = min(B, 128)
+        roots = base["tok"][:, 0].contiguous()
+        if nmodes == 1:
+            tb = tev.tev_build_tree(zb0, Kb, B, roots)
+
+            def fn_tb(j):
+                tev.tev_build_tree(zbring[j % len(zbring)], Kb, B, out=tb)
+        else:
+            tb = tev.tev_build_tree_modes(zb0, Kb, B, None, roots)
+
+            def fn_tb(j):
+                tev.tev_build_tree_modes(zbring[j % len(zbring)], Kb, B, None, out=tb)
         gs = []
         with torch.cuda.stream(stream):
             for j in range(n_multi):
@@ -536,15 +556,11 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         tb_us = a.elapsed_time(b) / (reps * G) * 1e3
-        del gs
-        tree_build = {"us": round(tb_us, 3), "K": Kb, "B": B, "rows": R * H, "vocab": V,
-                      "bytes": R * H * V * esz,
-                      "achieved_gbs": round(R * H * V * esz / (tb_us * 1e-6) / 1e9, 1)}
-        log(f"[bench] tev_build_tree over {R * H} draft rows (K={Kb}, B={B}): {tb_us:.2f} us")
-        log(f"[bench] tev_exit_loss over {R * H} draft rows: loss {exit_loss['loss']['us']:.2f} us, "
-            f"loss + grad {exit_loss['loss_and_grad']['us']:.2f} us "
-            f"({exit_loss['loss_and_grad']['achieved_gbs']:.0f} GB/s)")
-        del zring
+        del gs, zbring
+        rows = zb.shape[0] * nmodes * zb.shape[-2]
+        tree_build = {"us": round(tb_us, 3), "modes": nmodes, "K": Kb, "B": B, "rows": rows, "vocab": V,
+                      "call": "tev_build_tree" if nmodes == 1 else "tev_build_tree_modes"}
+        log(f"[bench] {tree_build['call']} over {rows} draft rows (K={Kb}, B={B}): {tb_us:.2f} us")
 
     work = algorithmic_work(wl)
     attn_hbm_bound = work["attn_bytes"] / HBM_PEAK_GBS > work["attn_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e3
