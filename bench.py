@@ -216,7 +216,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the verification stage "
-              "runs on a single device and this build has no multi-GPU path.", file=sys.stderr)
+              "runs on a single device; the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
