@@ -129,6 +129,38 @@ def cpu_baseline(wl, budget_s: float = 10.0):
                       f"+ one draw per request), {el_t:.1f} s, fp64, {threads} OpenMP threads"}
 
 
+def oracle_rows_us(wl, pd_uni, exit_nodes, n_layers, P_c, zrows, loss_w, tb_args, budget_s=2.0):
+    """The oracle of each widened row, timed on the host on the same inputs as
+    the GPU call beside it (repeated up to budget_s, at least once)."""
+    import numpy as np
+    import oracle
+
+    def timed(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or n >= 20:
+                return el / n * 1e6
+
+    out = {"tev_predraw": timed(lambda: oracle.predraw(wl.logits, wl.dtype, wl.parents, wl.tokens, pd_uni,
+                                                       wl.inv_temperature))}
+    kv_shape = (n_layers, wl.R, wl.Hkv, P_c + wl.B, wl.D)
+    kk = np.zeros(kv_shape, np.uint16 if wl.dtype == "bf16" else np.float32)
+    out["tev_commit_kv"] = timed(lambda: oracle.commit_kv(kk, kk, wl.parents, exit_nodes, P_c))
+    del kk
+    if zrows is not None and loss_w is not None:
+        out["tev_exit_loss"] = timed(lambda: oracle.exit_loss(zrows, wl.dtype, wl.parents, wl.tokens, loss_w))
+    if tb_args is not None:
+        z, dt, K, B, roots, modes = tb_args
+        if modes == 1:
+            out["tev_build_tree"] = timed(lambda: oracle.build_tree(z, dt, K, B, roots))
+        else:
+            out["tev_build_tree_modes"] = timed(lambda: oracle.build_tree_modes(z, dt, K, B, roots))
+    return {k: round(v, 1) for k, v in out.items()}
+
+
 def load_traffic(config: str, src_hash: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources."""
@@ -461,6 +493,8 @@ def main():
     # gradient), graphs of consecutive calls over a ring of draft-row copies
     exit_loss = None
     tree_build = None
+    loss_w_host = None
+    tb_args = None
     try:
         zrows = W.draft_rows(wl.name)
     except KeyError:
@@ -471,6 +505,7 @@ def main():
         zring = [z0] + [z0.clone() for _ in range(max(1, min(64, int(np.ceil(
             args.ring_bytes / (z0.numel() * z0.element_size()))))) - 1)]
         el_w = el_out.exit_mass.clone()
+        loss_w_host = el_w.cpu().numpy()
         ws_l = torch.empty(tev.tev_exit_loss_workspace_bytes(R, B, H, V), dtype=torch.uint8, device="cuda")
         lo = tev.ExitLossResult(torch.empty(1, dtype=torch.float32, device="cuda"),
                                 torch.empty((R, H), dtype=torch.float32, device="cuda"),
@@ -525,6 +560,7 @@ def main():
             args.ring_bytes / (zb0.numel() * zb0.element_size()))))) - 1)]
         Kb = min(B, 128)
         roots = base["tok"][:, 0].contiguous()
+        tb_args = (zb, wl.dtype, Kb, B, wl.tokens[:, 0].copy(), nmodes)
         if nmodes == 1:
             tb = tev.tev_build_tree(zb0, Kb, B, roots)
 
@@ -611,10 +647,41 @@ def main():
     roof["traffic"] = round(tk["bytes_per_launch"]) if tk else None
 
     cpu = None
+    rows_cpu = {}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         cpu = cpu_baseline(wl, args.cpu_seconds)
         log(f"[bench] oracle: {cpu['value']:.1f} nodes/s on {cpu['cores']} threads")
+        rows_cpu = oracle_rows_us(wl, pd_uni.cpu().numpy(), exit_nodes.cpu().numpy(), n_layers, P_c,
+                                  zrows, loss_w_host, tb_args)
+        log("[bench] oracle per widened call (us): " + ", ".join(f"{k} {v:.0f}" for k, v in rows_cpu.items()))
+
+    # The widened rows: GPU time, algorithmic bytes, what bounds them and the
+    # host oracle's time for the same call.
+    esz_l = 2 if wl.dtype == "bf16" else 4
+    nc = (V + 4095) // 4096
+    depth_mean = float(np.mean([W.depths_of(p).mean() for p in wl.parents]))
+    widened = {
+        "tev_predraw": {"us": per_call["tev_predraw"], "bound": "latency",
+                        "bytes": int(R * B * (nc * 24 + 4096 * esz_l))},
+        "tev_commit_kv": {"us": per_call["tev_commit_kv"], "bound": "latency",
+                          "bytes": int(4 * n_layers * R * wl.Hkv * (depth_mean + 1) * wl.D * esz_kv)},
+    }
+    if exit_loss is not None:
+        widened["tev_exit_loss"] = {"us": exit_loss["loss"]["us"], "bound": "hbm",
+                                    "bytes": exit_loss["loss"]["bytes"]}
+        widened["tev_exit_loss (with gradient)"] = {"us": exit_loss["loss_and_grad"]["us"], "bound": "hbm",
+                                                    "bytes": exit_loss["loss_and_grad"]["bytes"]}
+    if tree_build is not None:
+        widened[tree_build["call"]] = {"us": tree_build["us"], "bound": "latency",
+                                       "bytes": int(tree_build["rows"] * V * esz_l)}
+    for k_, e in widened.items():
+        e["us"] = round(e["us"], 3)
+        e["achieved_gbs"] = round(e["bytes"] / (e["us"] * 1e-6) / 1e9, 1)
+        e["frac_hbm"] = round(e["achieved_gbs"] / HBM_PEAK_GBS, 4)
+        base_k = k_.split(" ")[0]
+        if base_k in rows_cpu and k_ == base_k:
+            e["oracle_cpu_us"] = rows_cpu[base_k]
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
@@ -630,6 +697,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "widened_calls": widened,
         "kernel_source_hash": src_hash,
         "inputs": wl.digests(),
     }
