@@ -125,6 +125,16 @@ def _need_cuda(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous")
 
 
+def _need(t: torch.Tensor, dtype: torch.dtype, numel: int, name: str):
+    """A device tensor the kernels index by the call's sizes: the right element
+    type and exactly the right number of elements (the C ABI cannot see sizes)."""
+    _need_cuda(t)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
 # ---------------------------------------------------------------- exit law
 @dataclass
 class ExitLawResult:
@@ -146,8 +156,10 @@ def tev_exit_law(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tens
     parents/tokens int32 [R][B] on the GPU."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
-    _need_cuda(logits, parents, tokens)
+    _need_cuda(logits)
     R, B, V = logits.shape
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
     dev = logits.device
     L = lib()
     need = tev_exit_law_workspace_bytes(R, B, V)
@@ -158,6 +170,9 @@ def tev_exit_law(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tens
                             torch.empty((R, B), dtype=torch.float32, device=dev),
                             torch.empty((R, B), dtype=torch.float32, device=dev),
                             torch.empty((R,), dtype=torch.float32, device=dev), workspace)
+    for t, nm in ((out.rho, "rho"), (out.reach, "reach"), (out.exit_mass, "exit_mass")):
+        _need(t, torch.float32, R * B, nm)
+    _need(out.coverage, torch.float32, R, "coverage")
     st = L.tev_exit_law(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
                         float(inv_temperature), _p(out.rho), _p(out.reach), _p(out.exit_mass),
                         _p(out.coverage), _p(out.workspace), out.workspace.numel(), _stream())
@@ -171,14 +186,18 @@ def tev_sample(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor
     """TEV's exit-node and bonus-token draws; uniforms float32 [R][n][2]."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
-    _need_cuda(logits, parents, tokens, workspace, uniforms)
+    _need_cuda(logits, workspace, uniforms)
     R, B, V = logits.shape
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
     n = uniforms.shape[-2]
     if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * 2:
         raise ValueError("uniforms must be float32 [R][n][2]")
     if out is None:
         out = (torch.empty((R, n), dtype=torch.int32, device=logits.device),
                torch.empty((R, n), dtype=torch.int32, device=logits.device))
+    _need(out[0], torch.int32, R * n, "exit_node")
+    _need(out[1], torch.int32, R * n, "bonus_token")
     st = lib().tev_sample(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
                           float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
                           n, _p(out[0]), _p(out[1]), _stream())
@@ -193,8 +212,10 @@ def tev_predraw(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tenso
     Returns (node_draw [R][n][B], exit_node [R][n], bonus_token [R][n]), int32."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
-    _need_cuda(logits, parents, tokens, workspace, uniforms)
+    _need_cuda(logits, workspace, uniforms)
     R, B, V = logits.shape
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
     n = uniforms.shape[-2]
     if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * B:
         raise ValueError("uniforms must be float32 [R][n][B]")
@@ -202,6 +223,9 @@ def tev_predraw(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tenso
         out = (torch.empty((R, n, B), dtype=torch.int32, device=logits.device),
                torch.empty((R, n), dtype=torch.int32, device=logits.device),
                torch.empty((R, n), dtype=torch.int32, device=logits.device))
+    _need(out[0], torch.int32, R * n * B, "node_draw")
+    _need(out[1], torch.int32, R * n, "exit_node")
+    _need(out[2], torch.int32, R * n, "bonus_token")
     st = lib().tev_predraw(_p(logits), _dtype_code(logits), _p(parents), _p(tokens), R, B, V,
                            float(inv_temperature), _p(workspace), workspace.numel(), _p(uniforms),
                            n, _p(out[0]), _p(out[1]), _p(out[2]), _stream())
@@ -218,10 +242,13 @@ def tev_commit_kv(k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor, exit_
         k, v = k.unsqueeze(0), v.unsqueeze(0)
     L, R, Hkv, nkv, D = k.shape
     B = nkv - P
-    if v.shape != k.shape or v.dtype != k.dtype or parents.numel() != R * B or exit_node.numel() != R:
-        raise ValueError("k/v [L][R][Hkv][P+B][D], parents [R][B], exit_node [R]")
+    if v.shape != k.shape or v.dtype != k.dtype or B < 1:
+        raise ValueError("k/v [L][R][Hkv][P+B][D]")
+    _need(parents, torch.int32, R * B, "parents")
+    _need(exit_node, torch.int32, R, "exit_node")
     if out is None:
         out = torch.empty((R,), dtype=torch.int32, device=k.device)
+    _need(out, torch.int32, R, "new_len")
     st = lib().tev_commit_kv(_p(k), _p(v), _dtype_code(k), _p(parents), _p(exit_node), R, B, L, Hkv,
                              D, int(P), _p(out), _stream())
     _check("tev_commit_kv", st)
@@ -248,13 +275,12 @@ def tev_exit_loss(draft_logits: torch.Tensor, parents: torch.Tensor, tokens: tor
                   out: ExitLossResult | None = None) -> ExitLossResult:
     """Exit-guided draft-tree loss: draft_logits [R][H][V] (bf16 or f32),
     parents/tokens int32 [R][B], weights float32 [R][B], all on the GPU."""
-    _need_cuda(draft_logits, parents, tokens, weights)
+    _need_cuda(draft_logits)
     R, H, V = draft_logits.shape
     B = parents.shape[-1]
-    if parents.numel() != R * B or tokens.numel() != R * B or weights.numel() != R * B:
-        raise ValueError("parents, tokens and weights must be [R][B]")
-    if weights.dtype != torch.float32:
-        raise TypeError("weights must be float32")
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
+    _need(weights, torch.float32, R * B, "weights")
     dev = draft_logits.device
     if out is None:
         if workspace is None:
@@ -265,6 +291,11 @@ def tev_exit_loss(draft_logits: torch.Tensor, parents: torch.Tensor, tokens: tor
                              torch.empty((R, H), dtype=torch.float32, device=dev),
                              torch.empty((R, H, V), dtype=torch.float32, device=dev)
                              if with_grad else None, workspace)
+    _need(out.loss, torch.float32, 1, "loss")
+    _need(out.row_lse, torch.float32, R * H, "row_lse")
+    _need(out.row_weight, torch.float32, R * H, "row_weight")
+    if out.grad is not None:
+        _need(out.grad, torch.float32, R * H * V, "grad")
     st = lib().tev_exit_loss(_p(draft_logits), _dtype_code(draft_logits), _p(parents), _p(tokens),
                              _p(weights), R, B, H, V, _p(out.loss), _p(out.row_lse),
                              _p(out.row_weight), _p(out.grad), _p(out.workspace),
@@ -291,9 +322,9 @@ def tev_build_tree(draft_logits: torch.Tensor, K: int, B: int, root_tokens: torc
     """Best-first draft tree: draft_logits [R][L][V] (bf16 or f32) on the GPU,
     K tokens kept per position, B nodes (root included)."""
     _need_cuda(draft_logits)
-    if root_tokens is not None:
-        _need_cuda(root_tokens)
     R, L, V = draft_logits.shape
+    if root_tokens is not None:
+        _need(root_tokens, torch.int32, R, "root_tokens")
     dev = draft_logits.device
     if out is None:
         if workspace is None:
@@ -302,6 +333,9 @@ def tev_build_tree(draft_logits: torch.Tensor, K: int, B: int, root_tokens: torc
         out = BuiltTree(torch.empty((R, B), dtype=torch.int32, device=dev),
                         torch.empty((R, B), dtype=torch.int32, device=dev),
                         torch.empty((R, B), dtype=torch.float64, device=dev), workspace)
+    _need(out.parents, torch.int32, R * B, "parents")
+    _need(out.tokens, torch.int32, R * B, "tokens")
+    _need(out.scores, torch.float64, R * B, "scores")
     st = lib().tev_build_tree(_p(draft_logits), _dtype_code(draft_logits), _p(root_tokens), R, L, V, K, B,
                               _p(out.parents), _p(out.tokens), _p(out.scores), _p(out.workspace),
                               out.workspace.numel(), _stream())
@@ -319,10 +353,11 @@ def tev_build_tree_modes(draft_logits: torch.Tensor, K: int, B: int, log_prior: 
     """Merged heap over M draft modes: draft_logits [R][M][L][V] (bf16 or
     f32), log_prior float32 [R][M] or None (uniform)."""
     _need_cuda(draft_logits)
-    for t in (log_prior, root_tokens):
-        if t is not None:
-            _need_cuda(t)
     R, M, L, V = draft_logits.shape
+    if log_prior is not None:
+        _need(log_prior, torch.float32, R * M, "log_prior")
+    if root_tokens is not None:
+        _need(root_tokens, torch.int32, R, "root_tokens")
     dev = draft_logits.device
     if out is None:
         if workspace is None:
@@ -331,6 +366,9 @@ def tev_build_tree_modes(draft_logits: torch.Tensor, K: int, B: int, log_prior: 
         out = BuiltTree(torch.empty((R, B), dtype=torch.int32, device=dev),
                         torch.empty((R, B), dtype=torch.int32, device=dev),
                         torch.empty((R, B), dtype=torch.float64, device=dev), workspace)
+    _need(out.parents, torch.int32, R * B, "parents")
+    _need(out.tokens, torch.int32, R * B, "tokens")
+    _need(out.scores, torch.float64, R * B, "scores")
     st = lib().tev_build_tree_modes(_p(draft_logits), _dtype_code(draft_logits), _p(log_prior), _p(root_tokens),
                                     R, M, L, V, K, B, _p(out.parents), _p(out.tokens), _p(out.scores),
                                     _p(out.workspace), out.workspace.numel(), _stream())
@@ -347,11 +385,12 @@ def tev_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: to
                   P: int, scale: float | None = None, workspace: torch.Tensor | None = None,
                   out: torch.Tensor | None = None) -> torch.Tensor:
     """q [R][B][Hq][D], k/v [R][Hkv][P+B][D] (bf16 or f32) -> float32 [R][B][Hq][D]."""
-    _need_cuda(q, k, v, parents)
+    _need_cuda(q, k, v)
     R, B, Hq, D = q.shape
     Hkv = k.shape[1]
     if k.shape != (R, Hkv, P + B, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("k/v must be [R][Hkv][P+B][D] with q's dtype")
+    _need(parents, torch.int32, R * B, "parents")
     if scale is None:
         scale = 1.0 / float(np.sqrt(D))
     need = tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P)
@@ -359,6 +398,7 @@ def tev_tree_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: to
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((R, B, Hq, D), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, R * B * Hq * D, "out")
     st = lib().tev_tree_attn(_p(q), _p(k), _p(v), _dtype_code(q), _p(parents), R, B, Hq, Hkv, D,
                              int(P), float(scale), _p(out), _p(workspace), workspace.numel(),
                              _stream())
@@ -394,8 +434,10 @@ def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: 
     boundaries (tev_verify_round_timed)."""
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
-    _need_cuda(q, k, v, logits, parents, tokens, uniforms)
+    _need_cuda(q, k, v, logits, uniforms)
     R, B, Hq, D = q.shape
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
     Hkv = k.shape[1]
     V = logits.shape[-1]
     if k.shape != (R, Hkv, P + B, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -418,6 +460,12 @@ def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: 
                           torch.empty((R,), **f32),
                           torch.empty((R, n), dtype=torch.int32, device=dev),
                           torch.empty((R, n), dtype=torch.int32, device=dev), workspace)
+    _need(out.attn_out, torch.float32, R * B * Hq * D, "attn_out")
+    for t, nm in ((out.rho, "rho"), (out.reach, "reach"), (out.exit_mass, "exit_mass")):
+        _need(t, torch.float32, R * B, nm)
+    _need(out.coverage, torch.float32, R, "coverage")
+    _need(out.exit_node, torch.int32, R * n, "exit_node")
+    _need(out.bonus_token, torch.int32, R * n, "bonus_token")
     args = [_p(q), _p(k), _p(v), _p(logits), _dtype_code(q), _p(parents), _p(tokens), R, B, V, Hq,
             Hkv, D, int(P), float(scale), float(inv_temperature), _p(uniforms), n, _p(out.attn_out),
             _p(out.rho), _p(out.reach), _p(out.exit_mass), _p(out.coverage), _p(out.exit_node),
