@@ -464,118 +464,183 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
     }
 }
 
-// The merge across draft modes ("Multi-Future Drafting", App. B and Prop. 6):
-// every mode's emitted nodes, each mode in its own pop order, are taken in the
-// order in which the merged heap pops them (key, then depth, rank sequence,
-// mode).  The first entry of each distinct prefix creates a node (the prefix
-// is its parent's node and its token, looked up in an LDS hash table); a later
-// entry of the same prefix only maps its mode-local index to that node.  A
-// mode-local parent always precedes its children in the mode's order, so its
-// node is known.  One wave per request; lane k holds mode k's next entry.
-constexpr int TB_HASH = 1024;                    // >= 4 B slots: short probe chains
+// The merge across draft modes ("Multi-Future Drafting", App. B and Prop. 6).
+// The merged heap pops every mode's entries in that mode's own order, and all
+// entries together in one order: key, then depth, rank sequence, mode.  A
+// node is created at the first pop of each distinct prefix, in that order.
+// So the merge is a sort and a deduplication, done in parallel by one
+// workgroup per request:
+//   1. the entries' sort indices, bitonic-sorted in LDS by that order;
+//   2. canonical prefix ids, depth by depth: a prefix is (its parent's id,
+//      its token), inserted into an LDS hash table; a mode-local parent always
+//      has a smaller depth, so its id is known;
+//   3. the first sorted position of every prefix (LDS atomic minimum); the
+//      entries at their prefix's first position are the nodes, numbered by a
+//      block prefix sum in sorted order; the first B - 1 form the tree.
+constexpr int MG_THREADS = 1024;                     // one compare-exchange per thread and stage
+constexpr int MG_N = TB_MAX_MODES * TEV_MAX_NODES;   // entries, a power of two
+constexpr int MG_HASH = 2 * MG_N;                    // hash slots (load <= 1/2)
+constexpr int MG_ROOT = MG_HASH;                     // canonical id of the root prefix
+static_assert((MG_N & (MG_N - 1)) == 0, "bitonic sort over a power of two");
 
-__global__ __launch_bounds__(64) void k_tb_merge(const StreamRec *__restrict__ stream,
-                                                 const int32_t *__restrict__ stream_n,
-                                                 const unsigned *__restrict__ mode_status,
-                                                 const int32_t *__restrict__ root_tokens, int M, int B,
-                                                 unsigned *__restrict__ status, int32_t *__restrict__ parents,
-                                                 int32_t *__restrict__ tokens, double *__restrict__ scores) {
-    extern __shared__ StreamRec s_st[];              // M * B records
-    __shared__ int16_t s_map[TB_MAX_MODES * TEV_MAX_NODES];
-    __shared__ uint64_t s_hkey[TB_HASH];
-    __shared__ int s_hval[TB_HASH];
-    __shared__ int s_par[TEV_MAX_NODES], s_tok[TEV_MAX_NODES];
-    __shared__ double s_sc[TEV_MAX_NODES];
-    const int lane = threadIdx.x, r = blockIdx.x;
-    unsigned fl = 0u;
-    int len = 0;
-    if (lane < M) {
-        fl = mode_status[(size_t)r * M + lane];
-        len = stream_n[(size_t)r * M + lane];
+__global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__restrict__ stream,
+                                                         const int32_t *__restrict__ stream_n,
+                                                         const unsigned *__restrict__ mode_status,
+                                                         const int32_t *__restrict__ root_tokens, int M, int B,
+                                                         unsigned *__restrict__ status, int32_t *__restrict__ parents,
+                                                         int32_t *__restrict__ tokens, double *__restrict__ scores) {
+    constexpr int EPT = MG_N / MG_THREADS;            // sorted positions per thread
+    __shared__ double s_key[MG_N];
+    __shared__ uint64_t s_rhi[MG_N], s_rlo[MG_N];
+    __shared__ int s_tok[MG_N];
+    __shared__ int16_t s_par[MG_N], s_sidx[MG_N], s_cid[MG_N], s_pcid[MG_N], s_nid[MG_N];
+    __shared__ uint8_t s_dep[MG_N];
+    __shared__ uint64_t s_hkey[MG_HASH];
+    __shared__ int s_first[MG_HASH];
+    __shared__ int s_len[TB_MAX_MODES];
+    __shared__ int s_wsum[MG_THREADS / 64];
+    __shared__ unsigned s_fl;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = blockIdx.x;
+    const StreamRec *st = stream + (size_t)r * M * B;
+    if (tid == 0) s_fl = 0u;
+    if (tid < M) s_len[tid] = stream_n[(size_t)r * M + tid];
+    __syncthreads();
+    if (tid < M && mode_status[(size_t)r * M + tid] != 0u) atomicOr(&s_fl, (unsigned)TEV_FLAG_NONFINITE);
+    // entry e = k B + i, i in [1, len_k): mode k's i-th pop
+    for (int e = tid; e < MG_N; e += MG_THREADS) {
+        const int k = e / B, i = e - k * B;
+        const bool ok = e < M * B && i >= 1 && i < s_len[k];
+        if (ok) {
+            const StreamRec x = st[e];
+            s_key[e] = x.key;
+            s_rhi[e] = x.hi;
+            s_rlo[e] = x.lo;
+            s_tok[e] = x.token;
+            s_par[e] = (int16_t)x.parent;
+            s_dep[e] = (uint8_t)x.depth;
+        } else {
+            s_dep[e] = 0;
+        }
+        s_sidx[e] = (int16_t)(ok ? e : -1);
     }
-    fl = __ballot(fl != 0u) != 0ull ? (unsigned)TEV_FLAG_NONFINITE : 0u;
-    if (lane == 0) status[r] = fl;
+    for (int h = tid; h < MG_HASH; h += MG_THREADS) {
+        s_hkey[h] = 0ull;
+        s_first[h] = 0x7fffffff;
+    }
+    __syncthreads();
+    const unsigned fl = s_fl;
+    if (tid == 0) status[r] = fl;
     if (fl) {
-        for (int i = lane; i < B; i += 64) {
+        for (int i = tid; i < B; i += MG_THREADS) {
             parents[(size_t)r * B + i] = -1;
             tokens[(size_t)r * B + i] = -1;
             scores[(size_t)r * B + i] = __builtin_nan("");
         }
         return;
     }
-    for (int i = lane; i < M * B; i += 64) {
-        s_st[i] = stream[(size_t)r * M * B + i];       // entry 0 of a mode (the root) is not read
-        s_map[i] = (int16_t)((i % B) == 0 ? 0 : -1);   // every mode's root is node 0
+    // a before b in the merged heap's pop order; -1 (no entry) last
+    auto before_e = [&](int a, int b) __attribute__((always_inline)) {
+        if (a < 0) return false;
+        if (b < 0) return true;
+        const double ka = s_key[a], kb = s_key[b];
+        if (ka != kb) return ka > kb;
+        if (s_dep[a] != s_dep[b]) return s_dep[a] < s_dep[b];
+        if (s_rhi[a] != s_rhi[b]) return s_rhi[a] < s_rhi[b];
+        if (s_rlo[a] != s_rlo[b]) return s_rlo[a] < s_rlo[b];
+        return a / B < b / B;
+    };
+    // 1. bitonic sort of the entry indices, best first: pair p of a stage is
+    //    (i, i + j) with i = (p / j) 2j + p mod j
+    static_assert(MG_N == 2 * MG_THREADS, "one pair per thread");
+    for (int kk = 2; kk <= MG_N; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            const int i = 2 * tid - (tid & (j - 1));     // (tid / j) 2j + tid mod j, j a power of two
+            const int ij = i + j;
+            const int a = s_sidx[i], b = s_sidx[ij];
+            const bool up = (i & kk) == 0;
+            if (up ? before_e(b, a) : before_e(a, b)) {
+                s_sidx[i] = (int16_t)b;
+                s_sidx[ij] = (int16_t)a;
+            }
+            __syncthreads();
+        }
     }
-    for (int i = lane; i < TB_HASH; i += 64) s_hkey[i] = 0ull;
-    __syncthreads();
-    int idx = 1, n = 1;
-    while (n < B) {
-        const bool valid = lane < M && idx < len;
-        StreamRec e{0.0, 0ull, 0ull, 0, 0, 0, 0};
-        if (valid) e = s_st[lane * B + idx];
-        const float k32 = valid ? (float)e.key : -kInf;
-        const float m32 = wave::max_f32(k32);
-        uint64_t ball = __ballot(valid && k32 == m32);
-        if (ball == 0ull) break;                        // every stream is used up
-        int wl = __ffsll((long long)ball) - 1;
-        ball &= ball - 1;
-        if (ball) {                                     // key, depth, rank sequence, mode
-            double bk = wave::readlane_d(e.key, wl);
-            int bd = __builtin_amdgcn_readlane(e.depth, wl);
-            uint64_t bh = readlane_u64(e.hi, wl), bl = readlane_u64(e.lo, wl);
-            while (ball) {
-                const int l = __ffsll((long long)ball) - 1;
-                ball &= ball - 1;
-                const double k2 = wave::readlane_d(e.key, l);
-                const int d2 = __builtin_amdgcn_readlane(e.depth, l);
-                const uint64_t h2 = readlane_u64(e.hi, l), l2 = readlane_u64(e.lo, l);
-                const bool b = k2 != bk ? k2 > bk : d2 != bd ? d2 < bd : h2 != bh ? h2 < bh : l2 < bl;
-                if (b) {
-                    bk = k2; bd = d2; bh = h2; bl = l2;
-                    wl = l;
-                }
+    // 2. canonical prefix ids, one depth at a time
+    for (int d = 1; d <= TB_MAX_L; d++) {
+        for (int e = tid; e < M * B; e += MG_THREADS) {
+            if (s_dep[e] != d) continue;
+            const int k = e / B;
+            const int pl = s_par[e];
+            const int pc = pl == 0 ? MG_ROOT : s_cid[k * B + pl];
+            const uint64_t key = (((uint64_t)(uint32_t)pc << 32) | (uint32_t)s_tok[e]) + 1ull;
+            int h = (int)((key * 0x9E3779B97F4A7C15ull) >> 52) & (MG_HASH - 1);
+            for (;;) {
+                const uint64_t old = atomicCAS((unsigned long long *)&s_hkey[h], 0ull, (unsigned long long)key);
+                if (old == 0ull || old == key) break;
+                h = (h + 1) & (MG_HASH - 1);
             }
+            s_cid[e] = (int16_t)h;
+            s_pcid[e] = (int16_t)pc;
         }
-        const double key = wave::readlane_d(e.key, wl);
-        const int lpar = __builtin_amdgcn_readlane(e.parent, wl);
-        const int tok = __builtin_amdgcn_readlane(e.token, wl);
-        const int widx = __builtin_amdgcn_readlane(idx, wl);
-        const int P = s_map[wl * B + lpar];
-        // (parent node, token) -> node: linear probing
-        const uint64_t hk = (((uint64_t)(uint32_t)P << 32) | (uint32_t)tok) + 1ull;
-        int h = (int)((hk * 0x9E3779B97F4A7C15ull) >> 54);    // top 10 bits: TB_HASH = 1024
-        int found = -1;
-        for (;;) {
-            const uint64_t kk = s_hkey[h];
-            if (kk == 0ull) break;
-            if (kk == hk) {
-                found = s_hval[h];
-                break;
-            }
-            h = (h + 1) & (TB_HASH - 1);
-        }
-        int node = found;
-        if (found < 0) {
-            node = n;
-            if (lane == 0) {
-                s_hkey[h] = hk;
-                s_hval[h] = n;
-                s_par[n] = P;
-                s_tok[n] = tok;
-                s_sc[n] = key;
-            }
-            n++;
-        }
-        if (lane == 0) s_map[wl * B + widx] = (int16_t)node;
-        if (lane == wl) idx++;
+        __syncthreads();
+    }
+    // 3. first sorted position of every prefix, then the nodes in sorted order
+    for (int pos = tid; pos < MG_N; pos += MG_THREADS) {
+        const int e = s_sidx[pos];
+        if (e >= 0) atomicMin(&s_first[s_cid[e]], pos);
     }
     __syncthreads();
-    for (int i = lane; i < B; i += 64) {
-        const bool ok = i < n;
-        parents[(size_t)r * B + i] = (i == 0 || !ok) ? -1 : s_par[i];
-        tokens[(size_t)r * B + i] = i == 0 ? (root_tokens ? root_tokens[r] : 0) : (ok ? s_tok[i] : -1);
-        scores[(size_t)r * B + i] = i == 0 ? 0.0 : (ok ? s_sc[i] : __builtin_nan(""));
+    int cnt = 0;
+    bool first[EPT];
+#pragma unroll
+    for (int t = 0; t < EPT; t++) {
+        const int pos = tid * EPT + t;
+        const int e = s_sidx[pos];
+        first[t] = e >= 0 && s_first[s_cid[e]] == pos;
+        cnt += first[t] ? 1 : 0;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_up(incl, o);
+        if (lane >= o) incl += x;
+    }
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int base = incl - cnt;
+    for (int w = 0; w < wv; w++) base += s_wsum[w];
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < MG_THREADS / 64; w++) total += s_wsum[w];
+#pragma unroll
+    for (int t = 0; t < EPT; t++) {
+        const int pos = tid * EPT + t;
+        s_nid[pos] = (int16_t)(first[t] ? 1 + base : 0);
+        base += first[t] ? 1 : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < EPT; t++) {
+        const int pos = tid * EPT + t;
+        const int nid = s_nid[pos];
+        if (nid >= 1 && nid < B) {
+            const int e = s_sidx[pos];
+            const int pc = s_pcid[e];
+            parents[(size_t)r * B + nid] = pc == MG_ROOT ? 0 : s_nid[s_first[pc]];
+            tokens[(size_t)r * B + nid] = s_tok[e];
+            scores[(size_t)r * B + nid] = s_key[e];
+        }
+    }
+    for (int i = tid; i < B; i += MG_THREADS) {
+        if (i == 0) {
+            parents[(size_t)r * B] = -1;
+            tokens[(size_t)r * B] = root_tokens ? root_tokens[r] : 0;
+            scores[(size_t)r * B] = 0.0;
+        } else if (i > total) {                       // fewer distinct prefixes than nodes
+            parents[(size_t)r * B + i] = -1;
+            tokens[(size_t)r * B + i] = -1;
+            scores[(size_t)r * B + i] = __builtin_nan("");
+        }
     }
 }
 
@@ -616,7 +681,7 @@ hipError_t launch_typed(const void *z, const float *log_prior, double lp_default
     }
 #undef TB_HEAP
     if (M > 1)
-        k_tb_merge<<<R, 64, (size_t)M * B * sizeof(StreamRec), st>>>(strm, strm_n, hstatus, root_tokens, M, B,
+        k_tb_merge<<<R, MG_THREADS, 0, st>>>(strm, strm_n, hstatus, root_tokens, M, B,
                                                                       (unsigned *)(ws + MW.status), parents,
                                                                       tokens, scores);
     return hipGetLastError();
