@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
             }
 #pragma unroll
             for (int q = 0; q < SLOTS; q++)
-                if (q == bq) f[q] = sib;
+                if (q == wq) f[q] = sib;                 // wq is uniform: one branch taken
         }
         // node n's slot starts with its rank-0 child
         if (d < L && lane == (n & 63)) {
