@@ -370,7 +370,8 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
     // whose values are in units of 2^vst.
     auto spv = [&](f32x4 (&S)[NQT][KT], int t_stage, int vst) __attribute__((always_inline)) {
         const int kb = kbeg + t_stage * KS;
-        const bool masked = (kb + KS > P) || (kb + KS > kend);
+        const bool tree_keys = kb + KS > P;                  // stage holds tree rows
+        const bool past_end = kb + KS > kend;                // stage runs past the split
         const uint16_t *sv = s_v + (t_stage & 1) * STV;
         // accumulators into the units of this stage's V
         if (vst > vs_acc) {
@@ -382,8 +383,18 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
             vs_acc = vst;
         }
         // S[t][kt][i] is key kb + 16 kt + 4 grp + i; one branch for every tile
-        // (the key arithmetic stays inside it).
-        if (masked) {
+        // (the key arithmetic stays inside it).  A prefix stage that runs
+        // past its split only needs the range test.
+        if (!tree_keys && past_end) {
+#pragma unroll
+            for (int kt = 0; kt < KT; kt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const bool in_range = kb + 16 * kt + 4 * grp + i < kend;
+#pragma unroll
+                    for (int t = 0; t < NQT; t++) S[t][kt][i] = in_range ? S[t][kt][i] : -kInf;
+                }
+        } else if (tree_keys) {
 #pragma unroll
             for (int kt = 0; kt < KT; kt++)
 #pragma unroll
@@ -499,8 +510,14 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
     }
 #undef TEV_ATTN_STAGE
 
-    // Finalise: every lane of a query column holds the full sums.
+    // Finalise: every lane of a query column holds the full sums.  With
+    // splits, tile t of each wave is staged through LDS (the stage buffers are
+    // free after the last barrier; wave w owns rows [16 w, 16 w + 16) of
+    // buffer t) and written back as whole rows below.
     const size_t rows_all = (size_t)(n_wg / (row_blocks * splits)) * rows_total;
+    constexpr int RST = D + 8;          // staging row stride (elements)
+    static_assert(NQT <= 2 && NW * 16 * RST <= 2 * STK && NW * 16 * RST <= 2 * STV,
+                  "a wave's staged tiles fit the K and V stage buffers");
 #pragma unroll
     for (int t = 0; t < NQT; t++) {
         const float lt = accl[t][0];
@@ -532,17 +549,39 @@ __device__ __forceinline__ void attn_mfma_wg(const AttnArgs &A, const int task) 
             const int u = (mx > 0.f) ? min(max(ex - 15, -126), 127) : 0;
             const float sc = inv * __builtin_ldexpf(1.0f, -u);
             const size_t prow = (size_t)sp * rows_all + (size_t)rg * rows_total + row;
-            uint16_t *o16 = part_o + prow * D;
+            uint16_t *tile = (t == 0 ? s_k : s_v) + wave * 16 * RST;
 #pragma unroll
             for (int dt = 0; dt < DT; dt++) {
                 const f32x4 val = acc[t][dt] * sc;
                 f16x4 h;
 #pragma unroll
                 for (int j = 0; j < 4; j++) h[j] = (_Float16)val[j];
-                *reinterpret_cast<f16x4 *>(o16 + dt * 16 + grp * 4) = h;
+                *reinterpret_cast<f16x4 *>(tile + l16 * RST + dt * 16 + grp * 4) = h;
             }
             if (grp == 0)
                 *reinterpret_cast<f32x4 *>(part_ml + prow * 4) = f32x4{m_run[t], lt, (float)u, 0.f};
+        }
+    }
+    if (splits > 1) {
+        // Each store instruction writes four whole 2D-byte rows; the partials
+        // are read once, by the combine, so they are written as streaming
+        // (non-temporal) stores.  The staging writes above came from this
+        // wave, so in-order LDS access is the only ordering needed.
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int t = 0; t < NQT; t++) {
+            const uint16_t *tile = (t == 0 ? s_k : s_v) + wave * 16 * RST;
+#pragma unroll
+            for (int it = 0; it < D / 32; it++) {
+                const int idx = it * 64 + lane;
+                const int rr = idx / (D / 8), ch = idx % (D / 8);
+                const int row = wrow0 + t * 16 + rr;
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(tile + rr * RST + ch * 8);
+                if (row < rows_total) {
+                    const size_t prow = (size_t)sp * rows_all + (size_t)rg * rows_total + row;
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(part_o + prow * D + ch * 8));
+                }
+            }
         }
     }
 }
