@@ -66,6 +66,12 @@ SMALL = [
     dict(name="bf16_max_nodes", R=1, B=256, V=9000, Hq=4, Hkv=2, D=128, P=1024, tree="random"),
     dict(name="bf16_root_only", R=2, B=1, V=5000, Hq=4, Hkv=2, D=128, P=200, tree="random"),
     dict(name="f32_small", R=2, B=16, V=3000, Hq=4, Hkv=4, D=64, P=128, tree="random", dtype="f32"),
+    # the reach workgroups beside the attention for up to 7 and from 8
+    # requests on (the attention plan leaves that many CUs), and logit rows
+    # that are not whole 16-byte vectors
+    dict(name="bf16_r7", R=7, B=20, V=12000, Hq=4, Hkv=2, D=64, P=100, tree="random"),
+    dict(name="bf16_r9", R=9, B=20, V=12000, Hq=4, Hkv=2, D=64, P=100, tree="random"),
+    dict(name="bf16_odd_vocab", R=2, B=30, V=9001, Hq=4, Hkv=2, D=128, P=150, tree="random"),
 ]
 
 
