@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -83,10 +84,15 @@ ROUND_SOURCES = ("exit_law.hip", "exit_law_dev.h", "round.hip", "tev_internal.h"
 
 
 def kernel_source_hash() -> str:
+    """Hash of the code the round's kernels are compiled from, comments and
+    blank space left out (a comment edit does not change what was counted)."""
     h = hashlib.sha256()
     for f in ROUND_SOURCES:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(f.encode() + " ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -6,24 +6,23 @@
 // (itself included) of kv head g = h / G, G = Hq / Hkv; cache row P + j holds
 // tree node j.
 //
-// k_attn_mfma (bf16): one workgroup of eight waves serves up to 64 NQT query
+// k_attn_mfma (bf16): one workgroup of eight waves serves up to 128 NQT query
 // rows of one (request, kv head) -- the G*B rows (node i, head g*G + hh) share
 // that head's K/V, so the GQA group times the tree makes the products dense --
 // over one split of the prefix; the last split also takes the B tree rows
-// under the ancestor mask.  Four waves take the rows of the block, two key
-// groups take alternate 32-key blocks of each 64-key stage (two waves per
-// SIMD), and the groups' results are merged through LDS at the end.  K and V
-// stages sit row-major in LDS, double buffered, while the next stages' global
-// loads are in flight.  Scores are formed transposed,
-//   S^T (32 keys x 16 queries) = K (32 x D) . Q^T (D x 16),
+// under the ancestor mask.  Each wave owns 16 NQT rows for every 64-key stage
+// of the split.  K and V stages sit row-major in LDS, double buffered, while
+// the next stages' global loads are in flight.  Scores are formed transposed,
+//   S^T (16 keys x 16 queries per tile) = K (16 x D) . Q^T (D x 16),
 // with v_mfma_f32_16x16x32_bf16, so each lane holds one query column; its
-// online-softmax probabilities, split into bf16 hi + lo parts, are exactly the
-// B operand of
+// online-softmax probabilities, converted to fp16, are exactly the B operand of
 //   O^T (D x 16) += V^T (D x 32 keys) . P^T (32 keys x 16),
-// whose V^T operand comes straight from the row-major V stage through the
-// transposing LDS read, in the key order the score tiles leave in registers.
-// Tree rows are masked by a per-node ancestor bitmap in LDS (one bit per node).
-// Partial results of split prefixes are merged by k_attn_combine.
+// (v_mfma_f32_16x16x32_f16, V in fp16 under a per-workgroup power-of-two
+// scale) whose V^T operand comes straight from the row-major V stage through
+// the transposing LDS read, in the key order the score tiles leave in
+// registers.  Tree rows are masked by a per-node ancestor bitmap in LDS (one
+// bit per node).  Partial results of split prefixes are merged by
+// k_attn_combine.
 //
 // k_attn_alu (fp32): one wave per query row, lanes over head_dim, online
 // softmax in fp32 -- a plain vector-ALU kernel for fp32 inputs.
