@@ -530,7 +530,7 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
     __shared__ unsigned s_bits[SAMPLE_THREADS];
     const size_t kd = (size_t)r * n_draws + n;
 
-    // ---- round 1 ----
+    // ---- load round 1 ----
     const unsigned st = A.status[r];
     const double u1 = (double)A.uniforms[2 * kd];
     const double u2 = (double)A.uniforms[2 * kd + 1];
@@ -554,7 +554,7 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
         Vn = max(wave::max_i32(best), 0);
     }
 
-    // ---- round 2: the chunk whose running residual sum first exceeds u2 * T ----
+    // ---- load round 2: the chunk whose running residual sum first exceeds u2 * T ----
     const size_t rb = (size_t)r * B + Vn;
     const double *RC = rcum + rb * nc;
     const double t2 = u2 * RC[nc - 1];
@@ -572,7 +572,7 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
         cc = max(wave::max_i32(best), 0);
     }
 
-    // ---- round 3: the chunk ----
+    // ---- load round 3: the chunk ----
     const int c0 = cc * CHUNK;
     const int len = min(CHUNK, V - c0);
     const T *chunk = logits + rb * (size_t)V + c0;
