@@ -106,3 +106,25 @@ def test_round_invalid_tree_is_flagged():
     assert np.all(res.exit_node[1].cpu().numpy() == -1)
     assert np.all(np.isnan(res.attn_out[1].cpu().numpy()))
     assert np.all(np.isfinite(res.attn_out[0].cpu().numpy()))
+
+
+def test_round_timed_matches_round():
+    """tev_verify_round_timed (events at the launch boundaries, as bench.py
+    times the round) writes exactly what tev_verify_round writes, and its
+    events are recorded in launch order."""
+    wl = W.make_custom("round_timed", R=1, B=40, V=30000, dtype="bf16", tree="random", Hq=8, Hkv=2,
+                       D=128, P=600, n_uniform=4)
+    q, k, v = _dev(wl, wl.q), _dev(wl, wl.k), _dev(wl, wl.v)
+    lg, par, tok, uni = GP.device_inputs(wl)
+    args = (q, k, v, lg, par, tok, uni, wl.P, wl.scale, wl.inv_temperature)
+    ref = tev.tev_verify_round(*args)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    got = tev.tev_verify_round(*args, events=ev)
+    torch.cuda.synchronize()
+    for name in ("attn_out", "rho", "reach", "exit_mass", "coverage", "exit_node", "bonus_token"):
+        np.testing.assert_array_equal(getattr(got, name).cpu().numpy(), getattr(ref, name).cpu().numpy(),
+                                      err_msg=name)
+    gaps = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    assert all(g >= 0.0 for g in gaps), gaps
