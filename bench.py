@@ -100,7 +100,7 @@ def algorithmic_work(wl):
     """Bytes and FLOPs the method must move / compute per round (the dense
     work of masked sibling pairs is not counted)."""
     import numpy as np
-    from draft_tree_verification_amd import workloads as W
+    from tests import workloads as W
     e = 2 if wl.dtype == "bf16" else 4
     kv = 2 * wl.R * wl.Hkv * (wl.P + wl.B) * wl.D * e
     q = wl.R * wl.B * wl.Hq * wl.D * e
@@ -260,7 +260,7 @@ def main():
     import numpy as np
     import torch
     from draft_tree_verification_amd import tev
-    from draft_tree_verification_amd import workloads as W
+    from tests import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

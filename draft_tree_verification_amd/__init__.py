@@ -5,4 +5,4 @@ kernels for gfx950 behind a C ABI (``include/tev.h``).
 The binding lives in :mod:`draft_tree_verification_amd.tev`; importing this
 package does not load the native library.
 """
-__all__ = ["tev", "workloads"]
+__all__ = ["tev"]

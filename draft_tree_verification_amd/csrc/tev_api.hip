@@ -52,6 +52,12 @@ long long universe_size(int K, int L, long long cap) {
 
 tev_status hip_status(hipError_t e) { return e == hipSuccess ? TEV_OK : TEV_ERR_HIP; }
 
+// The attention kernels address one head's K / V extent, (P + B) rows of D
+// elements, with 32-bit byte offsets (buffer resources): it must stay below 2^31.
+bool kv_extent_ok(int P, int B, int D, int dtype) {
+    return ((long long)P + B) * D * (long long)esize(dtype) < (1LL << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,9 +229,10 @@ tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
     if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
     if (R < 1 || B < 1 || B > TEV_MAX_NODES || Hq < 1 || Hkv < 1 || P < 0) return TEV_ERR_SHAPE;
     if (Hq % Hkv) return TEV_ERR_SHAPE;
-    if ((long long)R * Hkv > 65535 || (long long)P + B > (1LL << 30)) return TEV_ERR_SHAPE;
+    if ((long long)R * Hkv > 65535) return TEV_ERR_SHAPE;
     if (D != 64 && D != 128) return TEV_ERR_UNSUPPORTED;
-    if (!isfinite(scale)) return TEV_ERR_VALUE;
+    if (!kv_extent_ok(P, B, D, dtype)) return TEV_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return TEV_ERR_VALUE;
     if (dtype == TEV_BF16 && (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16))
         return TEV_ERR_UNSUPPORTED;
     if (workspace_bytes < attn_ws_layout(R, B, Hq, Hkv, D, P).total) return TEV_ERR_WORKSPACE;
@@ -254,10 +261,11 @@ tev_status tev_verify_round_timed(const void *q, const void *k, const void *v, c
     tev_status s = check_exit_shape(R, B, V);
     if (s != TEV_OK) return s;
     if (Hq < 1 || Hkv < 1 || P < 0 || Hq % Hkv) return TEV_ERR_SHAPE;
-    if ((long long)R * Hkv > 65535 || (long long)P + B > (1LL << 30)) return TEV_ERR_SHAPE;
+    if ((long long)R * Hkv > 65535) return TEV_ERR_SHAPE;
     if (n_draws < 1 || n_draws > 65535) return TEV_ERR_SHAPE;
     if (D != 64 && D != 128) return TEV_ERR_UNSUPPORTED;
-    if (!isfinite(scale)) return TEV_ERR_VALUE;
+    if (!kv_extent_ok(P, B, D, dtype)) return TEV_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return TEV_ERR_VALUE;
     if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return TEV_ERR_VALUE;
     if (dtype == TEV_BF16 &&
         (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)attn_out) % 16))

@@ -156,7 +156,10 @@ tev_status tev_predraw(const void *logits, int dtype, const int32_t *parents,
  *       over j in {0..P-1} U {P + a : a on the root path of i}, with kv head
  *       g = h / (Hq / Hkv).
  * dtype TEV_BF16 (MFMA kernels, fp32 accumulation) or TEV_F32 (vector-ALU
- * kernel).  D must be 64 or 128; Hq % Hkv == 0; P >= 0; scale finite.
+ * kernel).  D must be 64 or 128; Hq % Hkv == 0; P >= 0; one head's K (and
+ * V) extent (P + B) * D * element size must be below 2^31 bytes (the kernels
+ * address it with 32-bit offsets), else TEV_ERR_SHAPE; scale must be finite
+ * and > 0 (1/sqrt(D) in every workload), else TEV_ERR_VALUE.
  * parents [R][B] as above (tokens are not needed).
  * workspace must hold tev_tree_attn_workspace_bytes(R, B, Hq, Hkv, D, P) bytes
  * (partial results of split-prefix launches and per-request status).
@@ -184,7 +187,8 @@ tev_status tev_tree_attn(const void *q, const void *k, const void *v, int dtype,
  * workspace: tev_sample, tev_export_exit_cdf and tev_export_residual_cdf
  * accept it after the round.  tev_read_device_status with kind 2 returns the
  * request's exit-law and attention flags together.
- * Errors: as the three calls (host checks before anything is enqueued).
+ * Errors: as the three calls (host checks before anything is enqueued),
+ * including the attention's limits on scale and on the K / V extent.
  * ------------------------------------------------------------------------ */
 size_t tev_verify_round_workspace_bytes(int R, int B, int V, int Hq, int Hkv, int D, int P);
 

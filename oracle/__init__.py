@@ -69,7 +69,7 @@ def _load():
         lib.oracle_exit_law.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, vp, vp, vp, ip]
         lib.oracle_sample.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, vp, ip, vp, vp, vp, ip]
         lib.oracle_residual_cdf.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp]
-        lib.oracle_predraw.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, ip, vp, vp, vp, vp, ip]
+        lib.oracle_predraw.argtypes = [vp, ip, vp, vp, ip, ip, ip, dp, vp, ip, vp, vp, vp, vp, vp, ip]
         lib.oracle_tree_attn.argtypes = [vp, vp, vp, ip, vp, ip, ip, ip, ip, ip, ip, dp, vp, vp,
                                          ctypes.c_int64, ip]
         lib.oracle_check_tree.argtypes = [vp, vp, ip, ip]
@@ -177,6 +177,7 @@ class PredrawDraws:
     exit_node: np.ndarray    # [R][n] int32
     bonus_token: np.ndarray  # [R][n] int32
     band: np.ndarray         # [R][n] bool: a draw on the walked path within 1e-6 of a boundary
+    node_band: np.ndarray    # [R][n][B] bool: node v's own draw within 1e-6 of a boundary of its bin
 
 
 def predraw(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndarray,
@@ -195,12 +196,13 @@ def predraw(logits: np.ndarray, dtype: str, parents: np.ndarray, tokens: np.ndar
     nd = np.empty((R, n, B), np.int32)
     en = np.empty((R, n), np.int32); bt = np.empty((R, n), np.int32)
     band = np.empty((R, n), np.uint8)
+    nband = np.empty((R, n, B), np.uint8)
     st = _load().oracle_predraw(_ptr(lg), _DTYPE_CODES[dtype], _ptr(par), _ptr(tok), R, B, V,
                                 float(inv_temperature), _ptr(u), n, _ptr(nd), _ptr(en), _ptr(bt),
-                                _ptr(band), int(nthreads))
+                                _ptr(band), _ptr(nband), int(nthreads))
     if st != 0:
         raise OracleError(f"oracle_predraw failed with status {st}")
-    return PredrawDraws(nd, en, bt, band.astype(bool))
+    return PredrawDraws(nd, en, bt, band.astype(bool), nband.astype(bool))
 
 
 def commit_kv(k: np.ndarray, v: np.ndarray, parents: np.ndarray, exit_node: np.ndarray, P: int):

@@ -164,6 +164,11 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
         }
         /* A(v): tokens of v's children. */
         unsigned char *in_A = (unsigned char *)calloc((size_t)V, 1);
+        if (!in_A) {
+#pragma omp critical
+            status = 4;
+            continue;
+        }
         int n_children = 0;
         long double child_sum = 0.0L;
         for (int u = 1; u < B; u++)
@@ -205,6 +210,7 @@ int oracle_exit_law(const void *logits, int dtype, const int32_t *parents, const
         }
         long double C = 0.0L, wsum = 0.0L, wdepth = 0.0L;
         int *depth = (int *)malloc(sizeof(int) * (size_t)B);
+        if (!depth) { status = 4; break; }
         tree_depths(par, B, depth);
         for (int v = 0; v < B; v++) {
             double w = P[v] * rho[(size_t)r * B + v];
@@ -301,6 +307,13 @@ int oracle_sample(const void *logits, int dtype, const int32_t *parents, const i
                                              : (const void *)((const uint16_t *)logits + (size_t)r * B * V);
         double *W = (double *)malloc(sizeof(double) * (size_t)B);
         double **res_cum = (double **)calloc((size_t)B, sizeof(double *)); /* built on first use */
+        if (!W || !res_cum) {
+            free(W);
+            free(res_cum);
+#pragma omp critical
+            status = 4;
+            continue;
+        }
         double run = 0.0;
         for (int j = 0; j < B; j++) { run += exit_mass[(size_t)r * B + j]; W[j] = run; }
         for (int n = 0; n < n_draws; n++) {
@@ -309,9 +322,16 @@ int oracle_sample(const void *logits, int dtype, const int32_t *parents, const i
             int Vn = inverse_cdf(W, B, u1, &band[2 * k]);
             if (!res_cum[Vn]) {
                 res_cum[Vn] = (double *)malloc(sizeof(double) * (size_t)V);
-                if (oracle_residual_cdf(rows, dtype, par, tok, B, V, Vn, inv_temperature, res_cum[Vn])) {
+                if (!res_cum[Vn]) {
 #pragma omp critical
-                    status = 5;
+                    status = 4;
+                    break;
+                }
+                int st = oracle_residual_cdf(rows, dtype, par, tok, B, V, Vn, inv_temperature, res_cum[Vn]);
+                if (st) {
+#pragma omp critical
+                    status = st;
+                    break;
                 }
             }
             exit_node[k] = Vn;
@@ -335,13 +355,15 @@ int oracle_sample(const void *logits, int dtype, const int32_t *parents, const i
  * Outputs: node_draw [R][n][B] (R_v, the inverse CDF of p_v in token order at
  * u), exit_node and bonus_token [R][n]; band [R][n] = 1 when the draw of any
  * node on the walked path lies within 1e-6 of a boundary of its bin (the
- * draws of nodes off the path cannot change the outcome).
+ * draws of nodes off the path cannot change the outcome); node_band
+ * [R][n][B] (or NULL) = 1 when node v's own draw lies within 1e-6 of a
+ * boundary of its bin.
  * Rows are processed one request at a time: B cumulative rows of V doubles.
  */
 int oracle_predraw(const void *logits, int dtype, const int32_t *parents, const int32_t *tokens,
                    int R, int B, int V, double inv_temperature, const float *uniforms,
                    int n_draws, int32_t *node_draw, int32_t *exit_node, int32_t *bonus_token,
-                   unsigned char *band, int nthreads) {
+                   unsigned char *band, unsigned char *node_band, int nthreads) {
     if (R < 1 || B < 1 || V < 1 || n_draws < 1 || !(inv_temperature > 0.0)) return 3;
     set_threads(nthreads);
     for (int r = 0; r < R; r++)
@@ -374,9 +396,11 @@ int oracle_predraw(const void *logits, int dtype, const int32_t *parents, const 
 #pragma omp parallel for schedule(dynamic, 16)
         for (int n = 0; n < n_draws; n++) {
             size_t k = (size_t)r * n_draws + n;
-            for (int v = 0; v < B; v++)
+            for (int v = 0; v < B; v++) {
                 node_draw[k * B + v] = inverse_cdf(cum + (size_t)v * V, V,
                                                    (double)uniforms[k * B + v], &nb[(size_t)n * B + v]);
+                if (node_band) node_band[k * B + v] = nb[(size_t)n * B + v];
+            }
             int v = 0;
             unsigned char on_band = 0;
             for (;;) {
@@ -421,6 +445,7 @@ int oracle_tree_attn(const void *q, const void *k, const void *v, int dtype, con
             if (par[i] < 0 || par[i] >= i) return 1;
     }
     int G = Hq / Hkv;
+    int status = 0;
     int64_t total = rows ? n_rows : (int64_t)R * B * Hq;
     size_t kv_rows = (size_t)P + B;
 #pragma omp parallel for schedule(dynamic, 4)
@@ -434,9 +459,16 @@ int oracle_tree_attn(const void *q, const void *k, const void *v, int dtype, con
         /* key set J(i): prefix rows, then the root path of i */
         int n_keys = P;
         int *keys = (int *)malloc(sizeof(int) * ((size_t)P + B));
+        double *s = (double *)malloc(sizeof(double) * ((size_t)P + B));
+        if (!keys || !s) {
+            free(keys);
+            free(s);
+#pragma omp critical
+            status = 4;
+            continue;
+        }
         for (int j = 0; j < P; j++) keys[j] = j;
         for (int a = i; a >= 0; a = par[a]) keys[n_keys++] = P + a;
-        double *s = (double *)malloc(sizeof(double) * (size_t)n_keys);
         size_t qoff = (((size_t)r * B + i) * Hq + h) * D;
         size_t kvbase = ((size_t)r * Hkv + g) * kv_rows * D;
         double smax = -INFINITY;
@@ -458,5 +490,5 @@ int oracle_tree_attn(const void *q, const void *k, const void *v, int dtype, con
         free(s);
         free(keys);
     }
-    return 0;
+    return status;
 }

@@ -146,3 +146,44 @@ def check_attn(wl, rows: np.ndarray | None = None, nthreads=0):
     worst = int(np.argmax(err))
     assert err.max() <= TOL_REL, f"row error {err.max():.3e} at row {worst if rows is None else rows[worst]}"
     return float(err.max())
+
+
+def request_rows(wl, requests) -> np.ndarray:
+    """Flat query-row indices ((r * B + i) * Hq + h) of every row of the given requests."""
+    per = wl.B * wl.Hq
+    return np.concatenate([np.arange(r * per, (r + 1) * per, dtype=np.int64) for r in requests])
+
+
+def check_draws_and_cdfs(wl, lg, par, tok, ws, exit_node, bonus, ora, cdf_nodes=3, s=None,
+                         nthreads=0):
+    """Draws of one round (exit_node, bonus [R][n]) against the oracle's on the
+    same uniforms outside the band, and the GPU's exit CDF (every request) and
+    residual CDFs (the most drawn nodes of up to two requests) within 1e-6 of
+    the oracle's, read from the exit-law workspace ``ws``."""
+    s = wl.inv_temperature if s is None else s
+    dr = oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, ora.exit_mass, wl.uniforms, s,
+                       nthreads=nthreads)
+    ok_e = ~dr.band_exit
+    ok_b = ok_e & ~dr.band_bonus
+    mism_e = np.argwhere(ok_e & (exit_node != dr.exit_node))
+    assert len(mism_e) == 0, f"exit node mismatches at {mism_e[:5].tolist()}"
+    mism_b = np.argwhere(ok_b & (bonus != dr.bonus_token))
+    assert len(mism_b) == 0, (f"bonus mismatches at {mism_b[:5].tolist()}: gpu "
+                              f"{bonus[tuple(mism_b[0])]} oracle {dr.bonus_token[tuple(mism_b[0])]}")
+    rep = {"band_excluded": int((~ok_b).sum()), "draws": int(ok_b.size)}
+    cdf_gpu = tev.tev_export_exit_cdf(ws, wl.R, wl.B, wl.V)
+    cum = np.cumsum(ora.exit_mass, axis=1)
+    rep["exit_cdf_dev"] = float(np.abs(cdf_gpu - cum / cum[:, -1:]).max())
+    assert rep["exit_cdf_dev"] < CDF_TOL, rep
+    dev = 0.0
+    for r in sorted({0, wl.R - 1}):
+        counts = np.bincount(dr.exit_node[r], minlength=wl.B)
+        for v in list(np.argsort(-counts)[:cdf_nodes]):
+            if ora.exit_mass[r, v] <= 0:
+                continue
+            ref = oracle.residual_cdf(wl.logits[r], wl.dtype, wl.parents[r], wl.tokens[r], int(v), s)
+            got = tev.tev_export_residual_cdf(lg, par, tok, ws, r, int(v), s).cpu().numpy()
+            dev = max(dev, float(np.abs(got - ref).max()))
+    rep["residual_cdf_dev"] = dev
+    assert dev < CDF_TOL, rep
+    return rep

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -85,6 +85,28 @@ def test_argument_errors_return_before_any_launch():
     assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, 4, 8, 2, 128, 100, float("inf"), fake, fake, need_a, s) == 8
     assert L.tev_tree_attn(fake, fake, fake, 1, null, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 1
     assert L.tev_tree_attn(fake, fake, fake, 5, fake, 1, 4, 8, 2, 128, 100, 0.1, fake, fake, need_a, s) == 3
+    # scale must be > 0 (every dtype): zero or negative scales are refused
+    for bad_scale in (0.0, -0.0, -0.1):
+        for dt in (0, 1):
+            assert L.tev_tree_attn(fake, fake, fake, dt, fake, 1, 4, 8, 2, 128, 100, bad_scale, fake, fake,
+                                   need_a, s) == 8, (bad_scale, dt)
+    # one head's K / V extent must stay below 2^31 bytes: (P + B) D e < 2^31
+    B = 4
+    p_max_bf16 = (1 << 31) // (128 * 2) - B - 1     # (P + B) 256 = 2^31 - 256: accepted
+    ws_big = 1 << 62
+    assert L.tev_tree_attn(fake, fake, fake, 1, fake, 1, B, 8, 2, 128, p_max_bf16 + 1, 0.1, fake, fake,
+                           ws_big, s) == 2                                          # exactly 2^31
+    assert L.tev_tree_attn(fake, fake, fake, 0, fake, 1, B, 8, 2, 128, (1 << 31) // 512 - B, 0.1, fake,
+                           fake, ws_big, s) == 2                                    # f32: 2^31
+    # the same limits through the whole round
+    need_r = L.tev_verify_round_workspace_bytes(1, 4, 1000, 8, 2, 128, 100)
+    assert need_r > 0
+    args = lambda dt, P, sc, ws: (fake, fake, fake, fake, dt, fake, fake, 1, 4, 1000, 8, 2, 128, P, sc, 1.0,
+                                  fake, 1, fake, fake, fake, fake, fake, fake, fake, fake, ws, s)
+    assert L.tev_verify_round(*args(1, 100, 0.0, need_r)) == 8
+    assert L.tev_verify_round(*args(1, 100, -1.0, need_r)) == 8
+    assert L.tev_verify_round(*args(1, p_max_bf16 + 1, 0.1, ws_big)) == 2
+    assert L.tev_verify_round(*args(1, 100, 0.1, need_r - 1)) == 5
     # exit-guided loss
     need_l = L.tev_exit_loss_workspace_bytes(2, 9, 4, 1000)
     assert need_l > 0 and L.tev_exit_loss_workspace_bytes(2, 9, 1025, 1000) == 0

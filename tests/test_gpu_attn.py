@@ -1,13 +1,13 @@
 """GPU parity of tev_tree_attn against the CPU oracle (through the C ABI).
 
-Small cases compare every row; the named workloads run at full size, in the
-launch configuration the benchmark times, and compare sampled rows (every head
-of a few nodes, plus random rows) that the oracle computes one by one."""
+Small cases and the named workloads compare every row (the named workloads at
+full size, in the launch configuration the benchmark times); the 32-request
+workload compares every row of its first and last request."""
 import numpy as np
 import pytest
 
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import gpu_parity as GP
 
 pytestmark = pytest.mark.gpu
@@ -37,31 +37,21 @@ def test_small_cases(case):
     GP.log(f"[attn] {name} ok max row error {err:.3e}")
 
 
-def _sample_rows(wl, n_random=48, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.integers(0, wl.R * wl.B * wl.Hq, size=n_random).tolist())
-    # every head of the root, the deepest node and a middle node of request 0 and R-1
-    d = W.depths_of(wl.parents[0])
-    for r in {0, wl.R - 1}:
-        for i in {0, int(np.argmax(d)), wl.B // 2, wl.B - 1}:
-            for h in range(wl.Hq):
-                rows.add((r * wl.B + i) * wl.Hq + h)
-    return np.array(sorted(rows), np.int64)
-
-
 @pytest.mark.parametrize("name", ["tiny", "qwen3_4b", "qwen3_8b_wide", "mixture"])
 def test_named_workloads(name):
-    GP.log(f"[attn] workload {name}")
+    """Every query row of the named workload at full size."""
+    GP.log(f"[attn] workload {name} (every row)")
     wl = W.make_config(name, n_uniform=1)
-    rows = None if name == "tiny" else _sample_rows(wl)
-    err = GP.check_attn(wl, rows=rows)
+    err = GP.check_attn(wl)
     GP.log(f"[attn] {name} ok max row error {err:.3e}")
 
 
 def test_batched_workload():
-    GP.log("[attn] workload batched (32 requests, P=32768)")
+    """The 32-request workload at full size (P = 32768 per request): every row
+    of the first and the last request."""
+    GP.log("[attn] workload batched (32 requests, P=32768): every row of requests 0 and 31")
     wl = W.make_config("batched", n_uniform=1)
-    err = GP.check_attn(wl, rows=_sample_rows(wl, n_random=64))
+    err = GP.check_attn(wl, rows=GP.request_rows(wl, [0, wl.R - 1]))
     GP.log(f"[attn] batched ok max row error {err:.3e}")
 
 

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 
 pytestmark = pytest.mark.gpu
 

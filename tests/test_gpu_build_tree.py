@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import gpu_parity as GP
 
 pytestmark = pytest.mark.gpu

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import gpu_parity as GP
 
 pytestmark = pytest.mark.gpu
@@ -29,10 +29,12 @@ def _check(wl, n=64, seed=0):
     torch.cuda.synchronize()
     nd, en, bt = nd.cpu().numpy(), en.cpu().numpy(), bt.cpu().numpy()
     ora = oracle.predraw(wl.logits, wl.dtype, wl.parents, wl.tokens, u, wl.inv_temperature)
-    # node draws: compare those whose uniform is not within 1e-6 of a boundary
-    # (the band of each node's own bin, from the oracle's row CDF)
+    # node draws: equal wherever the node's uniform is not within 1e-6 of a
+    # boundary of its bin (the oracle's per-node band, from its row CDF)
     same = nd == ora.node_draw
-    assert same.mean() > 0.999, f"{(~same).sum()} of {same.size} node draws differ"
+    mism = np.argwhere(~same & ~ora.node_band)
+    assert len(mism) == 0, (f"{len(mism)} node draws differ outside the band; first "
+                            f"{[(tuple(i), nd[tuple(i)], ora.node_draw[tuple(i)]) for i in mism[:5]]}")
     ok = ~ora.band
     np.testing.assert_array_equal(en[ok], ora.exit_node[ok])
     np.testing.assert_array_equal(bt[ok], ora.bonus_token[ok])
@@ -46,7 +48,7 @@ def _check(wl, n=64, seed=0):
                     break
                 v = nxt[0]
             assert en[r, d] == v and bt[r, d] == nd[r, d, v]
-    return int((~same).sum()), int((~ok).sum())
+    return int(ora.node_band.sum()), int((~ok).sum())
 
 
 CASES = [

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from draft_tree_verification_amd import tev
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import gpu_parity as GP
 
 pytestmark = pytest.mark.gpu
@@ -86,14 +86,46 @@ def test_round_small(case):
     GP.log(f"[round] {name} ok, attention row error {err:.3e}")
 
 
-@pytest.mark.parametrize("name", ["qwen3_4b", "mixture"])
+NAMED = ["tiny", "qwen3_4b", "qwen3_8b_wide", "mixture", "batched"]
+
+
+@pytest.mark.parametrize("name", NAMED)
 def test_round_named(name):
-    GP.log(f"[round] workload {name}")
-    wl = W.make_config(name, n_uniform=256)
-    rng = np.random.default_rng(1)
-    rows = np.unique(rng.integers(0, wl.R * wl.B * wl.Hq, size=64))
-    err = _check_round(wl, rows=rows)
-    GP.log(f"[round] {name} ok, attention row error {err:.3e}")
+    """Every named workload at full size through the call the benchmark times
+    (each runs its own attention plan and reach batching: at qwen3_8b_wide
+    two query tiles per wave with four reach batches, at batched 32 requests
+    with eight CUs left to the reach).  rho, P, w and C of every node, 4096
+    uniform pairs per request with the exit and residual CDF deviations, and
+    every attention row (at batched, every row of the first and the last
+    request); the exit law and draws also bit-equal to tev_exit_law +
+    tev_sample on the same inputs."""
+    GP.log(f"[round] workload {name} (full size, 4096 uniform pairs per request)")
+    wl = W.make_config(name, n_uniform=4096)
+    res, flags, (lg, par, tok, uni) = _run_round(wl)
+    assert np.all(flags == 0), flags
+    GP.log(f"[round] {name}: round done, comparing the exit law")
+    el = tev.tev_exit_law(lg, par, tok, wl.inv_temperature)
+    en, bt = tev.tev_sample(lg, par, tok, el.workspace, uni, wl.inv_temperature)
+    torch.cuda.synchronize()
+    for nm, a, b in (("rho", res.rho, el.rho), ("reach", res.reach, el.reach),
+                     ("exit_mass", res.exit_mass, el.exit_mass), ("coverage", res.coverage, el.coverage),
+                     ("exit_node", res.exit_node, en), ("bonus_token", res.bonus_token, bt)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy(), err_msg=nm)
+    ora = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature)
+    rep = {k: GP.assert_close_rel(k, getattr(res, a).cpu().numpy(), getattr(ora, b))
+           for k, a, b in (("rho", "rho", "rho"), ("reach", "reach", "reach"),
+                           ("exit_mass", "exit_mass", "exit_mass"), ("coverage", "coverage", "coverage"))}
+    rep.update(GP.check_draws_and_cdfs(wl, lg, par, tok, res.workspace, res.exit_node.cpu().numpy(),
+                                       res.bonus_token.cpu().numpy(), ora,
+                                       cdf_nodes=2 if wl.R > 1 else 3))
+    GP.log(f"[round] {name}: exit law and draws ok {rep}; comparing attention")
+    rows = GP.request_rows(wl, sorted({0, wl.R - 1})) if name == "batched" else None
+    ref = oracle.tree_attn(wl.q, wl.k, wl.v, wl.dtype, wl.parents, wl.P, wl.scale, rows=rows)
+    got = res.attn_out.cpu().numpy().reshape(-1, wl.D)
+    got = got if rows is None else got[rows]
+    err = GP.attn_row_errors(got, ref)
+    assert err.max() <= GP.TOL_REL, f"attention row error {err.max():.3e} at row {int(np.argmax(err))}"
+    GP.log(f"[round] {name} ok: {len(err)} attention rows, max row error {err.max():.3e}")
 
 
 def test_round_invalid_tree_is_flagged():

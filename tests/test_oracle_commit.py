@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 
 
 def _case(seed, R=2, B=23, Hq=4, Hkv=2, D=64, P=37, L=2):

@@ -19,7 +19,7 @@ import scipy.special
 import torch
 
 import oracle
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 
 
 def _case(seed, R=3, B=19, V=41, extra_rows=1, scale=3.0):

@@ -10,7 +10,7 @@ import torch
 from scipy.special import softmax
 
 import oracle
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import lawtools as LT
 
 

@@ -10,7 +10,7 @@ import pytest
 from scipy.special import logsumexp, softmax
 
 import oracle
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import lawtools as LT
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")

@@ -8,7 +8,7 @@ import pytest
 from scipy.special import softmax
 
 import oracle
-from draft_tree_verification_amd import workloads as W
+from tests import workloads as W
 from tests import lawtools as LT
 
 
@@ -45,11 +45,41 @@ def test_node_draws_are_the_library_inverse_cdf():
             uu = float(u[0, n, v])
             j = int(np.searchsorted(c, uu * c[-1], side="right"))
             lo = 0.0 if j == 0 else cn[j - 1]
-            if abs(uu - lo) < 1e-6 or abs(uu - cn[j]) < 1e-6:
+            in_band = abs(uu - lo) < 1e-6 or abs(uu - cn[j]) < 1e-6
+            if in_band:
                 continue
+            assert not dr.node_band[0, n, v], (v, n)
             assert dr.node_draw[0, n, v] == j, (v, n)
             checked += 1
     assert checked > 0.99 * B * u.shape[1]
+
+
+def test_walk_band_is_the_band_of_the_walked_draws():
+    """The walk's band flag is set exactly when some node on the walked path
+    (root to exit node) has its own draw in the band; draws off the path do
+    not count.  Uniforms are placed on bin boundaries on purpose."""
+    rng = np.random.default_rng(21)
+    B, V = 12, 40
+    parents, tokens = W.random_tree(B, V, rng)
+    lg = (rng.standard_normal((B, V)) * 1.5).astype(np.float32)
+    for u_ in range(1, B):
+        lg[parents[u_], tokens[u_]] += 2.0
+    u = _uniforms(22, 1, 300, B)
+    p = softmax(lg.astype(np.float64), axis=1)
+    cn = np.cumsum(p, axis=1)
+    cn /= cn[:, -1:]
+    # every fifth draw: put some node's uniform on a boundary of its row CDF
+    for n in range(0, u.shape[1], 5):
+        v = int(rng.integers(0, B))
+        u[0, n, v] = np.float32(cn[v, int(rng.integers(0, V - 1))])
+    dr = oracle.predraw(lg, "f32", parents, tokens, u)
+    assert dr.node_band.any()
+    for n in range(u.shape[1]):
+        path, v = [], int(dr.exit_node[0, n])
+        while v >= 0:
+            path.append(v)
+            v = int(parents[v]) if v > 0 else -1
+        assert dr.band[0, n] == bool(dr.node_band[0, n, path].any()), n
 
 
 def test_root_only_tree_is_plain_sampling():
