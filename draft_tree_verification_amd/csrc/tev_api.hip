@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "exit_loss.h"
 #include "tev_internal.h"
 #include "tree_build.h"
@@ -56,6 +58,30 @@ tev_status hip_status(hipError_t e) { return e == hipSuccess ? TEV_OK : TEV_ERR_
 // elements, with 32-bit byte offsets (buffer resources): it must stay below 2^31.
 bool kv_extent_ok(int P, int B, int D, int dtype) {
     return ((long long)P + B) * D * (long long)esize(dtype) < (1LL << 31);
+}
+
+// Device scratch of tev_verify_round_noalloc: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host-
+// side stand-in, never the device memory: kernels and copies receive the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[TEV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept.  NULL on a HIP error.
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -289,6 +315,30 @@ tev_status tev_verify_round(const void *q, const void *k, const void *v, const v
                                   scale, inv_temperature, uniforms, n_draws, attn_out, rho, reach,
                                   exit_mass, coverage, exit_node, bonus_token, workspace,
                                   workspace_bytes, stream, nullptr);
+}
+
+tev_status tev_verify_round_noalloc(const void *q, const void *k, const void *v,
+                                    const void *logits, int dtype, const int32_t *parents,
+                                    const int32_t *tokens, int R, int B, int V, int Hq, int Hkv,
+                                    int D, int P, float scale, float inv_temperature,
+                                    const float *uniforms, int n_draws, float *attn_out, float *rho,
+                                    float *reach, float *exit_mass, float *coverage,
+                                    int32_t *exit_node, int32_t *bonus_token, void *stream) {
+    if (!q || !k || !v || !logits || !parents || !tokens || !uniforms || !attn_out || !rho ||
+        !reach || !exit_mass || !coverage || !exit_node || !bonus_token)
+        return TEV_ERR_NULL;
+    const size_t need = tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P);
+    if (need == 0) return TEV_ERR_SHAPE;
+    if (need > (size_t)TEV_NOALLOC_SCRATCH_BYTES) return TEV_ERR_WORKSPACE;
+    // Remaining argument checks run in the round itself, before any launch;
+    // the scratch address is looked up only once they could pass.
+    if (!dtype_ok(dtype)) return TEV_ERR_DTYPE;
+    void *ws = scratch_on_current_device();
+    if (!ws) return TEV_ERR_HIP;
+    return tev_verify_round_timed(q, k, v, logits, dtype, parents, tokens, R, B, V, Hq, Hkv, D, P,
+                                  scale, inv_temperature, uniforms, n_draws, attn_out, rho, reach,
+                                  exit_mass, coverage, exit_node, bonus_token, ws,
+                                  (size_t)TEV_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 tev_status tev_validate_tree_host(const int32_t *parents_host, const int32_t *tokens_host, int B,

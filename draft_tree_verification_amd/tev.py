@@ -33,7 +33,8 @@ EXPORTED = ["tev_exit_law_workspace_bytes", "tev_exit_law", "tev_sample",
             "tev_export_residual_cdf", "tev_verify_round_workspace_bytes", "tev_verify_round",
             "tev_verify_round_timed", "tev_predraw", "tev_commit_kv",
             "tev_exit_loss_workspace_bytes", "tev_exit_loss", "tev_build_tree_workspace_bytes",
-            "tev_build_tree", "tev_build_tree_modes_workspace_bytes", "tev_build_tree_modes"]
+            "tev_build_tree", "tev_build_tree_modes_workspace_bytes", "tev_build_tree_modes",
+            "tev_verify_round_noalloc"]
 
 
 class TevError(RuntimeError):
@@ -82,9 +83,12 @@ def lib() -> ctypes.CDLL:
         L.tev_verify_round.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.tev_verify_round_timed.argtypes = L.tev_verify_round.argtypes + [vp]
+        L.tev_verify_round_noalloc.argtypes = [vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i,
+                                               vp, vp, vp, vp, vp, vp, vp, vp]
         for fn in ("tev_exit_law", "tev_sample", "tev_predraw", "tev_commit_kv", "tev_exit_loss", "tev_build_tree",
                    "tev_build_tree_modes",
-                   "tev_tree_attn", "tev_validate_tree_host",
+                   "tev_tree_attn", "tev_validate_tree_host", "tev_verify_round", "tev_verify_round_timed",
+                   "tev_verify_round_noalloc",
                    "tev_read_device_status", "tev_export_exit_cdf", "tev_export_residual_cdf"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -478,6 +482,57 @@ def tev_verify_round(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: 
         st = lib().tev_verify_round_timed(*args, ctypes.cast(handles, ctypes.c_void_p))
         _check("tev_verify_round_timed", st)
     return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TEV_NOALLOC_SCRATCH_BYTES in include/tev.h
+
+
+def tev_verify_round_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, logits: torch.Tensor,
+                             parents: torch.Tensor, tokens: torch.Tensor, uniforms: torch.Tensor, P: int,
+                             scale: float | None = None, inv_temperature: float = 1.0,
+                             out: RoundResult | None = None) -> RoundResult:
+    """tev_verify_round on the library's own device scratch (no workspace
+    argument; the C call allocates nothing).  ``out`` may carry preallocated
+    outputs; its workspace field is ignored and returned as None."""
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    _need_cuda(q, k, v, logits, uniforms)
+    R, B, Hq, D = q.shape
+    _need(parents, torch.int32, R * B, "parents")
+    _need(tokens, torch.int32, R * B, "tokens")
+    Hkv = k.shape[1]
+    V = logits.shape[-1]
+    if k.shape != (R, Hkv, P + B, D) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k/v must be [R][Hkv][P+B][D] with q's dtype")
+    if logits.shape != (R, B, V) or logits.dtype != q.dtype:
+        raise ValueError("logits must be [R][B][V] with q's dtype")
+    n = uniforms.shape[-2]
+    if uniforms.dtype != torch.float32 or uniforms.numel() != R * n * 2:
+        raise ValueError("uniforms must be float32 [R][n][2]")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(D))
+    dev = q.device
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = RoundResult(torch.empty((R, B, Hq, D), **f32), torch.empty((R, B), **f32),
+                          torch.empty((R, B), **f32), torch.empty((R, B), **f32),
+                          torch.empty((R,), **f32),
+                          torch.empty((R, n), dtype=torch.int32, device=dev),
+                          torch.empty((R, n), dtype=torch.int32, device=dev), None)
+    _need(out.attn_out, torch.float32, R * B * Hq * D, "attn_out")
+    for t, nm in ((out.rho, "rho"), (out.reach, "reach"), (out.exit_mass, "exit_mass")):
+        _need(t, torch.float32, R * B, nm)
+    _need(out.coverage, torch.float32, R, "coverage")
+    _need(out.exit_node, torch.int32, R * n, "exit_node")
+    _need(out.bonus_token, torch.int32, R * n, "bonus_token")
+    st = lib().tev_verify_round_noalloc(
+        _p(q), _p(k), _p(v), _p(logits), _dtype_code(q), _p(parents), _p(tokens), R, B, V, Hq, Hkv, D,
+        int(P), float(scale), float(inv_temperature), _p(uniforms), n, _p(out.attn_out), _p(out.rho),
+        _p(out.reach), _p(out.exit_mass), _p(out.coverage), _p(out.exit_node), _p(out.bonus_token),
+        _stream())
+    _check("tev_verify_round_noalloc", st)
+    return RoundResult(out.attn_out, out.rho, out.reach, out.exit_mass, out.coverage, out.exit_node,
+                       out.bonus_token, None)
 
 
 # ---------------------------------------------------------------- helpers

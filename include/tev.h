@@ -10,7 +10,9 @@
  *  - Every array pointer is a DEVICE pointer owned by the caller unless its
  *    comment says "host".  The library never allocates, frees or retains
  *    memory, and holds no global mutable state: calls are reentrant, and
- *    calls on different workspaces may run concurrently.
+ *    calls on different workspaces may run concurrently.  The one exception
+ *    is tev_verify_round_noalloc, whose workspace is a library-owned device
+ *    array (see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call enqueues its kernels on `stream` and returns without
  *    synchronising, except the calls marked "synchronous".
@@ -51,6 +53,10 @@ extern "C" {
 #endif
 
 #define TEV_MAX_NODES 256
+
+/* Bytes of the device scratch array behind tev_verify_round_noalloc (32 MiB
+ * per GPU, held from the first such call on a GPU until the process ends). */
+#define TEV_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum {
     TEV_OK = 0,
@@ -199,6 +205,30 @@ tev_status tev_verify_round(const void *q, const void *k, const void *v, const v
                             float *attn_out, float *rho, float *reach, float *exit_mass,
                             float *coverage, int32_t *exit_node, int32_t *bonus_token,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* tev_verify_round for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs, but no workspace argument.
+ * Its workspace is a file-scope device array of TEV_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, whose address the first call on a GPU looks up (with that
+ * GPU current) and keeps; the call itself allocates nothing.  `stream` must
+ * belong to the current device.
+ * Errors: as tev_verify_round; TEV_ERR_WORKSPACE when
+ * tev_verify_round_workspace_bytes(R, B, V, Hq, Hkv, D, P) exceeds
+ * TEV_NOALLOC_SCRATCH_BYTES (checked before anything else touches the GPU);
+ * TEV_ERR_HIP if the array's address cannot be obtained.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the round needs no zeroed workspace, so nothing is cleared):
+ * calls that overlap on one GPU -- on different streams, or from several
+ * host threads -- race and must not be issued.  Device flags stay in the
+ * array; a flagged request shows as NaN / -1 outputs. */
+tev_status tev_verify_round_noalloc(const void *q, const void *k, const void *v,
+                                    const void *logits, int dtype, const int32_t *parents,
+                                    const int32_t *tokens, int R, int B, int V, int Hq, int Hkv,
+                                    int D, int P, float scale, float inv_temperature,
+                                    const float *uniforms, int n_draws, float *attn_out,
+                                    float *rho, float *reach, float *exit_mass, float *coverage,
+                                    int32_t *exit_node, int32_t *bonus_token, void *stream);
 
 /* tev_verify_round, and for profiling: events[0..3] (hipEvent_t, created by
  * the caller, any entry may be NULL) are recorded on `stream` before the

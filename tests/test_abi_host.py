@@ -107,6 +107,16 @@ def test_argument_errors_return_before_any_launch():
     assert L.tev_verify_round(*args(1, 100, -1.0, need_r)) == 8
     assert L.tev_verify_round(*args(1, p_max_bf16 + 1, 0.1, ws_big)) == 2
     assert L.tev_verify_round(*args(1, 100, 0.1, need_r - 1)) == 5
+    # the round on the library's scratch: a request whose workspace would
+    # exceed the scratch array is refused before anything touches the GPU
+    big = L.tev_verify_round_workspace_bytes(64, 256, 1 << 20, 8, 2, 128, 100)
+    assert big > tev.NOALLOC_SCRATCH_BYTES
+    na = lambda R, B, V: (fake, fake, fake, fake, 1, fake, fake, R, B, V, 8, 2, 128, 100, 0.1, 1.0, fake, 1,
+                          fake, fake, fake, fake, fake, fake, fake, s)
+    assert L.tev_verify_round_noalloc(*na(64, 256, 1 << 20)) == 5
+    assert L.tev_verify_round_noalloc(*na(1, 0, 1000)) == 2
+    assert L.tev_verify_round_noalloc(fake, fake, null, fake, 1, fake, fake, 1, 4, 1000, 8, 2, 128, 100, 0.1,
+                                      1.0, fake, 1, fake, fake, fake, fake, fake, fake, fake, s) == 1
     # exit-guided loss
     need_l = L.tev_exit_loss_workspace_bytes(2, 9, 4, 1000)
     assert need_l > 0 and L.tev_exit_loss_workspace_bytes(2, 9, 1025, 1000) == 0
