@@ -123,6 +123,7 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
     wave::lds_sync();
     bool dup = false;
     int mine_o[NPLV];   // half offset of child 1 + lane + 64 k, or -1
+    float cval[NPLV];   // that child's logit, loaded now (behind the part's own loads)
 #pragma unroll
     for (int k = 0; k < NPLV; k++) {
         // the test is evaluated outside the branch, so that the tree loads
@@ -131,6 +132,10 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
         const int o = ctok[k] - h0;
         const bool hit = (1 + lane + 64 * k < B) & (cpar[k] == v) & (o >= 0) & (o < len);
         mine_o[k] = hit ? o : -1;
+        // unconditional load of a valid address (the row's first logit when
+        // there is no hit), in flight with the part's loads instead of costing
+        // a memory round trip after the sums
+        cval[k] = to_f32<T>(logits[(size_t)rv * (size_t)V + (hit ? h0 + o : 0)]);
         if (hit) {
             const int kk = o / SPAN, rem = o - kk * SPAN;
             const int bitpos = kk * VW + (rem % VW);           // 0..EPW-1 within the owner lane
@@ -223,8 +228,7 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_vocab(
 #pragma unroll
         for (int k = 0; k < NPLV; k++) {
             if (mine_o[k] >= 0) {
-                const float xl = to_f32<T>(row[mine_o[k]]);
-                const float t = (mc > -kInf) ? __builtin_amdgcn_exp2f(fmaf(xl, sL, -Mc)) : 0.f;
+                const float t = (mc > -kInf) ? __builtin_amdgcn_exp2f(fmaf(cval[k], sL, -Mc)) : 0.f;
                 W.cterm[(size_t)r * B + 1 + lane + 64 * k] = make_float2(t, Mc);
             }
         }
