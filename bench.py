@@ -225,6 +225,292 @@ def summarize_counters(config: str, fetch_db: str, write_db: str):
     print(json.dumps(out, indent=1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_single_thread(wl_main, budget_s: float = 20.0):
+    """The oracle on one thread: whole rounds of the tiny and the main
+    workload, and the exit law alone on every workload (the 32-request one
+    on its first four requests), each timed once."""
+    import numpy as np
+    import oracle
+    from tests import workloads as W
+    out = {"threads": 1}
+
+    def one_round(wl):
+        u1 = np.ascontiguousarray(wl.uniforms[:, :1, :])
+        t0 = time.perf_counter()
+        oracle.tree_attn(wl.q, wl.k, wl.v, wl.dtype, wl.parents, wl.P, wl.scale, nthreads=1)
+        el = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature, nthreads=1)
+        oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, el.exit_mass, u1, wl.inv_temperature,
+                      nthreads=1)
+        return time.perf_counter() - t0
+
+    t_start = time.perf_counter()
+    rounds = {}
+    for wl in (W.make_config("tiny", n_uniform=1), wl_main):
+        dt = one_round(wl)
+        rounds[wl.name] = {"s_per_round": round(dt, 4), "nodes_per_s": round(wl.R * wl.B / dt, 2)}
+    out["round"] = rounds
+    exit_law = {}
+    for name in ("tiny", "qwen3_4b", "qwen3_8b_wide", "mixture", "batched"):
+        if time.perf_counter() - t_start > budget_s:
+            break
+        wl = W.make_config(name, n_uniform=1, with_attention=False,
+                           requests=4 if name == "batched" else None)
+        t0 = time.perf_counter()
+        oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature, nthreads=1)
+        dt = time.perf_counter() - t0
+        exit_law[name] = {"rows": wl.R * wl.B, "s": round(dt, 4), "rows_per_s": round(wl.R * wl.B / dt, 1)}
+    out["exit_law"] = exit_law
+    out["note"] = ("one OpenMP thread; the round is attention + exit law + one draw per request; "
+                   "the 32-request workload's exit law on its first 4 requests")
+    return out
+
+
+def timed_graphs(torch, stream, graphs, n_rounds, G, ring):
+    """Replay graphs of G rounds (then one-round graphs) for exactly n_rounds,
+    an event pair around each replay: (mean us per round, list of us per round
+    of each G-round replay)."""
+    per = []
+    evs = []
+    full, rest = divmod(n_rounds, G)
+    with torch.cuda.stream(stream):
+        e_all0 = torch.cuda.Event(enable_timing=True)
+        e_all1 = torch.cuda.Event(enable_timing=True)
+        e_all0.record(stream)
+        for i in range(full):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graphs["multi"][i % len(graphs["multi"])].replay()
+            b.record(stream)
+            evs.append((a, b))
+        for i in range(rest):
+            graphs["single"][(full * G + i) % ring].replay()
+        e_all1.record(stream)
+    torch.cuda.synchronize()
+    for a, b in evs:
+        per.append(a.elapsed_time(b) * 1e3 / G)
+    return e_all0.elapsed_time(e_all1) * 1e3 / n_rounds, per
+
+
+def percentiles(xs):
+    import numpy as np
+    if not xs:
+        return None
+    q = np.percentile(np.asarray(xs), [10, 50, 90])
+    return {"p10": round(float(q[0]), 3), "median": round(float(q[1]), 3), "p90": round(float(q[2]), 3),
+            "n": len(xs)}
+
+
+def measure_workload(name, steps, ring_bytes, log_prefix="[bench]"):
+    """Round time, launch intervals and roofline fractions of tev_verify_round
+    on one named workload (graphs of consecutive rounds on distinct input
+    copies, as for the headline workload)."""
+    import numpy as np
+    import torch
+    from draft_tree_verification_amd import tev
+    from tests import workloads as W
+    t_gen = time.perf_counter()
+    wl = W.make_config(name, n_uniform=1)
+    gen_s = time.perf_counter() - t_gen
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    base = dict(lg=to_dev(wl.logits), q=to_dev(wl.q), k=to_dev(wl.k), v=to_dev(wl.v),
+                par=tev.to_device_i32(wl.parents), tok=tev.to_device_i32(wl.tokens),
+                uni=torch.from_numpy(np.ascontiguousarray(wl.uniforms[:, :1, :])).cuda())
+    slot_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    ring = max(1, min(64, int(np.ceil(ring_bytes / slot_bytes))))
+    slots = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(ring - 1)]
+    R, B, V = wl.R, wl.B, wl.V
+    ws = torch.zeros(tev.tev_verify_round_workspace_bytes(R, B, V, wl.Hq, wl.Hkv, wl.D, wl.P),
+                     dtype=torch.uint8, device="cuda")
+    out = tev.tev_verify_round(base["q"], base["k"], base["v"], base["lg"], base["par"], base["tok"],
+                               base["uni"], wl.P, wl.scale, wl.inv_temperature, workspace=ws)
+
+    def step(s, events=None):
+        tev.tev_verify_round(s["q"], s["k"], s["v"], s["lg"], s["par"], s["tok"], s["uni"], wl.P, wl.scale,
+                             wl.inv_temperature, out=out, events=events)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    G = max(1, min(11, ring))
+    graphs = {"single": [], "multi": []}
+    with torch.cuda.stream(stream):
+        for s in slots:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(s)
+            graphs["single"].append(g)
+        for j in range(max(1, ring // G)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for t in range(G):
+                    step(slots[(j * G + t) % ring])
+            graphs["multi"].append(g)
+        for i in range(2):
+            graphs["multi"][i % len(graphs["multi"])].replay()
+    torch.cuda.synchronize()
+    mean_us, per = timed_graphs(torch, stream, graphs, steps, G, ring)
+    ev = [[HipEvent() for _ in range(4)] for _ in range(max(4, min(steps, 2 * ring)) + 2)]
+    with torch.cuda.stream(stream):
+        for i, row in enumerate(ev):
+            step(slots[i % ring], events=row)
+    torch.cuda.synchronize()
+    names = ("k_vocab", "k_round_attn", "k_round_tail")
+    phase = {nm: float(np.mean([HipEvent.elapsed_us(row[j], row[j + 1]) for row in ev[2:]]))
+             for j, nm in enumerate(names)}
+    work = algorithmic_work(wl)
+    attn_hbm = work["attn_bytes"] / HBM_PEAK_GBS > work["attn_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e3
+    vg = work["exit_law_bytes"] / (phase["k_vocab"] * 1e-6) / 1e9
+    if attn_hbm:
+        a = work["attn_bytes"] / (phase["k_round_attn"] * 1e-6) / 1e9
+        attn = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
+    else:
+        a = work["attn_flops"] / (phase["k_round_attn"] * 1e-6) / 1e12
+        attn = {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+    res = {"requests": R, "nodes_per_request": B, "vocab": V, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+           "head_dim": wl.D, "kv_prefix": wl.P, "ring_copies": ring, "rounds": steps,
+           "us_per_round": round(mean_us, 3), "round_us": percentiles(per),
+           "nodes_per_s": round(R * B / (mean_us * 1e-6), 1),
+           "launch_us": {k: round(v, 3) for k, v in phase.items()},
+           "vocab": {"bytes": work["exit_law_bytes"], "achieved_gbs": round(vg, 1),
+                     "frac_hbm": round(vg / HBM_PEAK_GBS, 4)},
+           "attention": dict(attn, bytes=work["attn_bytes"], flops=work["attn_flops"]),
+           "inputs": wl.digests()}
+    log(f"{log_prefix} {name}: {mean_us:.2f} us per round ({R * B / mean_us:.3f} M nodes/s), launches "
+        + ", ".join(f"{k} {v:.2f}" for k, v in phase.items()) + f" us (inputs generated in {gen_s:.1f} s)")
+    del graphs, slots, base, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def verifier_stage(budgets, n_layers=36, iters=100):
+    """TEV's decision (exit node + bonus, one draw) against predraw-and-follow
+    (B node draws + walk), each followed by the cache commit of the accepted
+    path over an n_layers cache, on the Qwen3-4B-shaped round at several node
+    budgets (both after the same exit law)."""
+    import numpy as np
+    import torch
+    from draft_tree_verification_amd import tev
+    from tests import workloads as W
+    res = {}
+    stream = torch.cuda.Stream()
+    for B in budgets:
+        wl = W.make_qwen_budget(B)
+        lg0 = torch.from_numpy(np.ascontiguousarray(wl.logits).view(np.int16)).view(torch.bfloat16).cuda()
+        ring = max(1, min(33, int(np.ceil(1.2e9 / (lg0.numel() * 2)))))
+        lgs = [lg0] + [lg0.clone() for _ in range(ring - 1)]
+        par, tok = tev.to_device_i32(wl.parents), tev.to_device_i32(wl.tokens)
+        uni = torch.from_numpy(np.ascontiguousarray(wl.uniforms[:, :1, :])).cuda()
+        pd_uni = torch.from_numpy((np.random.default_rng(7).integers(0, 1 << 24, size=(1, 1, B))
+                                   * 2.0 ** -24).astype(np.float32)).cuda()
+        el = tev.tev_exit_law(lg0, par, tok, wl.inv_temperature)
+        draws = tev.tev_sample(lg0, par, tok, el.workspace, uni, wl.inv_temperature)
+        pd = tev.tev_predraw(lg0, par, tok, el.workspace, pd_uni, wl.inv_temperature)
+        kc = torch.zeros((n_layers, 1, wl.Hkv, wl.P + B, wl.D), dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        exit_nodes = draws[0][:, 0].contiguous()
+        new_len = torch.empty((1,), dtype=torch.int32, device="cuda")
+        calls = {
+            "tev_sample": lambda j: tev.tev_sample(lgs[j % ring], par, tok, el.workspace, uni, wl.inv_temperature,
+                                                   out=draws),
+            "tev_predraw": lambda j: tev.tev_predraw(lgs[j % ring], par, tok, el.workspace, pd_uni,
+                                                     wl.inv_temperature, out=pd),
+            "tev_commit_kv": lambda j: tev.tev_commit_kv(kc, vc, par, exit_nodes, wl.P, out=new_len),
+        }
+        G = 11
+        us = {}
+        for name, fn in calls.items():
+            gs = []
+            with torch.cuda.stream(stream):
+                for j in range(max(1, ring // G)):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        for t in range(G):
+                            fn(j * G + t)
+                    gs.append(g)
+                for i in range(2):
+                    gs[i % len(gs)].replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            reps = max(1, iters // G)
+            with torch.cuda.stream(stream):
+                a.record(stream)
+                for i in range(reps):
+                    gs[i % len(gs)].replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us[name] = a.elapsed_time(b) / (reps * G) * 1e3
+            del gs
+        tev_stage = us["tev_sample"] + us["tev_commit_kv"]
+        pd_stage = us["tev_predraw"] + us["tev_commit_kv"]
+        res[f"B={B}"] = {"tev_sample_us": round(us["tev_sample"], 3), "tev_predraw_us": round(us["tev_predraw"], 3),
+                         "tev_commit_kv_us": round(us["tev_commit_kv"], 3),
+                         "tev_stage_us": round(tev_stage, 3), "predraw_stage_us": round(pd_stage, 3),
+                         "tev_reduction": round(1.0 - tev_stage / pd_stage, 4)}
+        log(f"[bench] verifier stage at B={B}: TEV {tev_stage:.2f} us vs predraw {pd_stage:.2f} us "
+            f"({100 * (1 - tev_stage / pd_stage):.1f}% lower; commit over {n_layers} layers)")
+        del lgs, kc, vc, el, draws, pd
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    res["note"] = ("both after the same tev_exit_law; decision (one draw per request) plus the cache "
+                   f"commit over {n_layers} layers of the 32/8-head, 4096-prefix cache; Qwen3-4B-shaped "
+                   "round cut at each node budget")
+    return res
+
+
+def device_peaks():
+    """Context: a 1 GiB device copy (read + write), a 1 GiB read (sum), and
+    a bf16 8192^3 GEMM, on this GPU."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    f = src.view(torch.float32)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda")
+
+    def t(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    copy_s = t(lambda: dst.copy_(src), 10)
+    read_s = t(lambda: f.sum(), 10)
+    gemm_s = t(lambda: torch.matmul(a, b), 10)
+    out = {"copy_1gib_gbs": round(2 * n / copy_s / 1e9, 1), "read_1gib_gbs": round(n / read_s / 1e9, 1),
+           "gemm_bf16_8192_tflops": round(2 * 8192 ** 3 / gemm_s / 1e12, 1),
+           "note": "torch copy_ (bytes read + written), torch sum of f32 (bytes read), torch.matmul bf16; "
+                   "context for the 8 TB/s and 2.5 PFLOP/s spec peaks"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +532,8 @@ def main():
                          "databases (FETCH_SIZE run, WRITE_SIZE run) of a --counters run")
     ap.add_argument("--separate", action="store_true",
                     help="time the three calls tev_tree_attn, tev_exit_law, tev_sample instead of tev_verify_round")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads, the verifier-stage comparison and the device peaks")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -402,7 +690,12 @@ def main():
 
     ms_per_step = timed(run_steps, args.steps)
     value = R * B / (ms_per_step * 1e-3)
-    log(f"[bench] {ms_per_step * 1e3:.2f} us per round -> {value / 1e6:.3f} M nodes/s")
+    # spread: one event pair around each G-round graph replay of a second pass
+    _, per_round = timed_graphs(torch, stream, {"multi": g_multi, "single": g_step}, args.steps, G, ring)
+    round_pct = percentiles(per_round)
+    log(f"[bench] {ms_per_step * 1e3:.2f} us per round -> {value / 1e6:.3f} M nodes/s"
+        + (f" (per-graph median {round_pct['median']:.2f}, p10 {round_pct['p10']:.2f}, p90 {round_pct['p90']:.2f})"
+           if round_pct else ""))
     ms_single = timed(lambda n: [g_step[i % ring].replay() for i in range(n)], args.steps)
     log(f"[bench] {ms_single * 1e3:.2f} us per round with one graph launch per round")
 
@@ -652,15 +945,35 @@ def main():
     tk = traffic.get("kernels", {}).get(dominant) if traffic else None
     roof["traffic"] = round(tk["bytes_per_launch"]) if tk else None
 
+    extra = {}
+    if not args.no_extra:
+        del slots, g_step, g_multi
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extra["verifier_stage"] = verifier_stage((32, 64, 128))
+        extra["device_peaks"] = device_peaks()
+        log(f"[bench] device peaks: {extra['device_peaks']}")
+        wls = {}
+        for name, st_ in (("qwen3_8b_wide", 50), ("mixture", 50), ("batched", 10)):
+            wls[name] = measure_workload(name, min(args.steps, st_), args.ring_bytes)
+        extra["workloads"] = wls
+
     cpu = None
     rows_cpu = {}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         cpu = cpu_baseline(wl, args.cpu_seconds)
-        log(f"[bench] oracle: {cpu['value']:.1f} nodes/s on {cpu['cores']} threads")
+        cpu["cpu_model"] = cpu_model()
+        log(f"[bench] oracle: {cpu['value']:.1f} nodes/s on {cpu['cores']} threads ({cpu['cpu_model']})")
         rows_cpu = oracle_rows_us(wl, pd_uni.cpu().numpy(), exit_nodes.cpu().numpy(), n_layers, P_c,
                                   zrows, loss_w_host, tb_args)
         log("[bench] oracle per widened call (us): " + ", ".join(f"{k} {v:.0f}" for k, v in rows_cpu.items()))
+        if not args.no_extra:
+            import oracle
+            n_thr = oracle.max_threads(0)
+            cpu["single_thread"] = oracle_single_thread(wl)
+            oracle.max_threads(n_thr)
+            log(f"[bench] oracle on one thread: {cpu['single_thread']}")
 
     # The widened rows: GPU time, algorithmic bytes, what bounds them and the
     # host oracle's time for the same call.
@@ -700,10 +1013,12 @@ def main():
                    "call": "tev_tree_attn + tev_exit_law + tev_sample" if args.separate
                    else "tev_verify_round", "rounds_per_graph": G},
         "ms_per_step_one_graph_per_round": round(ms_single, 6),
+        "round_us": round_pct,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "widened_calls": widened,
+        **extra,
         "kernel_source_hash": src_hash,
         "inputs": wl.digests(),
     }

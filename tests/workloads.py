@@ -31,6 +31,8 @@ from __future__ import annotations
 
 import hashlib
 import heapq
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -257,17 +259,34 @@ def _normal_store(rng: np.random.Generator, shape, dtype: str, scale: float = 1.
     return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
+def _pool_map(fn, items):
+    """Map over independent seeded items on a few threads (numpy's generators
+    and array arithmetic release the GIL); each item has its own seed, so the
+    result does not depend on the number of threads."""
+    items = list(items)
+    workers = min(len(items), max(1, min(16, len(os.sched_getaffinity(0)))))
+    if workers <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
 def make_attention(cfg: int, R: int, B: int, Hq: int, Hkv: int, D: int, P: int, dtype: str):
     """Q, K, V ~ N(0, 1) per request and kv head; cache rows P..P+B-1 are the tree nodes."""
     st = np.float32 if dtype == "f32" else np.uint16
     q = np.empty((R, B, Hq, D), st)
     k = np.empty((R, Hkv, P + B, D), st)
     v = np.empty((R, Hkv, P + B, D), st)
-    for r in range(R):
-        q[r] = _normal_store(_rng(cfg, r, S_Q), (B, Hq, D), dtype)
-        for g in range(Hkv):
+
+    def fill(item):
+        r, g = item
+        if g < 0:
+            q[r] = _normal_store(_rng(cfg, r, S_Q), (B, Hq, D), dtype)
+        else:
             k[r, g] = _normal_store(_rng(cfg, r, S_K, g), (P + B, D), dtype)
             v[r, g] = _normal_store(_rng(cfg, r, S_V, g), (P + B, D), dtype)
+
+    _pool_map(fill, [(r, g) for r in range(R) for g in range(-1, Hkv)])
     return q, k, v
 
 
@@ -426,25 +445,42 @@ def make_config(name: str, n_uniform: int = 4096, with_attention: bool = True,
     tok = np.empty((R, B), np.int32)
     st = np.float32 if dtype == "f32" else np.uint16
     logits = np.empty((R, B, V), st)
-    for r in range(R):
+    if name not in ("tiny", "qwen3_4b", "batched", "qwen3_8b_wide", "mixture"):
+        raise KeyError(name)
+
+    def request(r):
         if name == "tiny":
             p, t, lg = _request_tiny(cfg, r)
         elif name in ("qwen3_4b", "batched"):
             p, t, lg = _request_qwen_peaked(cfg, r, B)
         elif name == "qwen3_8b_wide":
             p, t, lg = _request_wide_zipf(cfg, r, B)
-        elif name == "mixture":
-            p, t, lg = _request_mixture(cfg, r, B)
         else:
-            raise KeyError(name)
+            p, t, lg = _request_mixture(cfg, r, B)
         if len(p) != B:
             raise RuntimeError(f"{name}: builder returned {len(p)} nodes, expected {B}")
         par[r], tok[r], logits[r] = p, t, lg
+
+    _pool_map(request, range(R))
     uni = np.stack([uniforms_for(cfg, r, n_uniform) for r in range(R)])
     w = Workload(name, cfg, R, B, V, dtype, logits, par, tok, uni, Hq, Hkv, D, P)
     if with_attention:
         w.q, w.k, w.v = make_attention(cfg, R, B, Hq, Hkv, D, P, dtype)
     w.meta["description"] = DESCRIPTIONS[name]
+    return w
+
+
+def make_qwen_budget(B: int, n_uniform: int = 1) -> Workload:
+    """The Qwen3-4B-shaped round at another node budget B (root included):
+    the same seeds, draft rows and target recipe as "qwen3_4b" (which is B =
+    64), the best-first tree cut at B nodes; logits only (no attention).  The
+    node budgets 32 / 64 / 128 are those of the pages' verifier-stage
+    comparison."""
+    cfg, _, _, V, dtype, Hq, Hkv, D, P = CONFIGS["qwen3_4b"]
+    p, t, lg = _request_qwen_peaked(cfg, 0, B)
+    w = Workload(f"qwen3_4b_B{B}", cfg, 1, B, V, dtype, lg[None], p[None].astype(np.int32),
+                 t[None].astype(np.int32), uniforms_for(cfg, 0, n_uniform)[None], Hq, Hkv, D, P)
+    w.meta["description"] = f"1 request, B={B} best-first over 16 peaked draft positions, V={V} bf16"
     return w
 
 
