@@ -127,7 +127,7 @@ def cpu_baseline(wl, budget_s: float = 10.0):
         oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, el.exit_mass, u1, wl.inv_temperature)
         rounds += 1
         el_t = time.perf_counter() - t0
-        if el_t >= budget_s or rounds >= 50:
+        if el_t >= budget_s or rounds >= 500:
             break
     nodes = rounds * wl.R * wl.B
     return {"value": nodes / el_t, "unit": "nodes/s", "cores": threads, "kind": "oracle",
@@ -220,6 +220,66 @@ def summarize_counters(config: str, fetch_db: str, write_db: str):
         out["kernels"][short(k)] = {"fetch_kib": fetch[k], "write_kib": write.get(k), "fetch_bytes": fb,
                                     "write_bytes": wb, "bytes_per_launch": fb + wb}
     path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+N_XCD = 8                 # XCDs of one MI355X (GRBM_GUI_ACTIVE is summed over them)
+N_SIMD = 256 * 4          # SIMDs of one MI355X
+
+
+def summarize_pmc(config: str, dbs):
+    """Per-launch counters of a --counters run (several rocprofv3 --pmc
+    databases, one pass each), with the calibration copy's readings, into
+    profiles/pmc_<config>.json; derived: MFMA busy fraction, MFMA FLOP and
+    rate, LDS bytes read, HBM bytes by FETCH_SIZE (scaled by the copy) and by
+    the L2's read requests and misses."""
+    import sqlite3
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    for db in dbs:
+        con = sqlite3.connect(db)
+        for name, disp, ctr, val in con.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            acc[name][ctr][disp] += val
+    short = lambda k: k.replace("void ", "").replace("tev::(anonymous namespace)::", "").split("(")[0]
+    mean = {k: {c: sum(d.values()) / len(d) for c, d in cs.items()} for k, cs in acc.items()}
+    # the calibration copy is the largest dispatch of the copy kernel (the
+    # same kernel also moves the run's small inputs)
+    peak = {k: {c: max(d.values()) for c, d in cs.items()} for k, cs in acc.items()}
+    copy_k = max((k for k in peak if "copy" in k.lower()), key=lambda k: peak[k].get("FETCH_SIZE", 0.0),
+                 default=None)
+    cal = peak.get(copy_k, {}) if copy_k else {}
+    out = {"kernel_source_hash": kernel_source_hash(), "workload": config, "calibration_kernel": short(copy_k or ""),
+           "calibration_bytes": COPY_BYTES, "calibration": cal, "kernels": {}}
+    for k, c in mean.items():
+        sk = short(k)
+        if not sk.startswith("k_"):
+            continue
+        d = {"counters": c}
+        if "GRBM_GUI_ACTIVE" in c:
+            cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+            d["cycles"] = cyc
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                d["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD)
+            if "SQ_LDS_IDX_ACTIVE" in c:
+                d["lds_active_frac"] = c["SQ_LDS_IDX_ACTIVE"] / (cyc * 256)
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        if mops:
+            d["mfma_flop"] = mops * 512
+        if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in c:
+            d["lds_read_bytes"] = c["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64
+        if "FETCH_SIZE" in c and cal.get("FETCH_SIZE"):
+            d["fetch_bytes"] = c["FETCH_SIZE"] * COPY_BYTES / cal["FETCH_SIZE"]
+        if "WRITE_SIZE" in c and cal.get("WRITE_SIZE"):
+            d["write_bytes"] = c["WRITE_SIZE"] * COPY_BYTES / cal["WRITE_SIZE"]
+        if "TCC_EA0_RDREQ_sum" in c and cal.get("TCC_EA0_RDREQ_sum"):
+            d["fetch_bytes_by_rdreq"] = c["TCC_EA0_RDREQ_sum"] * COPY_BYTES / cal["TCC_EA0_RDREQ_sum"]
+        if "TCC_MISS_sum" in c and cal.get("TCC_MISS_sum"):
+            d["fetch_bytes_by_l2_miss"] = c["TCC_MISS_sum"] * COPY_BYTES / cal["TCC_MISS_sum"]
+        out["kernels"][sk] = d
+    path = os.path.join(ROOT, "profiles", f"pmc_{config}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -530,6 +590,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "databases (FETCH_SIZE run, WRITE_SIZE run) of a --counters run")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
+                    help="write profiles/pmc_<workload>.json from the rocprofv3 --pmc databases "
+                         "(one per counter pass) of a --counters run")
     ap.add_argument("--separate", action="store_true",
                     help="time the three calls tev_tree_attn, tev_exit_law, tev_sample instead of tev_verify_round")
     ap.add_argument("--no-extra", action="store_true",
@@ -538,6 +601,9 @@ def main():
 
     if args.summarize_counters:
         summarize_counters(args.config, *args.summarize_counters)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.config, args.summarize_pmc)
         return
 
     if args.gpus != 1:

@@ -111,14 +111,20 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
     char *ws_e = ws + RL.exit;
     char *ws_a = ws + RL.attn;
     if (dtype != TEV_BF16) {
-        // fp32 attention runs on the vector ALU path: the three calls in order
+        // fp32 attention runs on the vector ALU path: the three calls in
+        // order (events: before the exit law, after it, after the attention,
+        // after the draws)
+        mark(0);
         hipError_t e = launch_exit_law(logits, dtype, vec, parents, tokens, R, B, V, sL, rho, reach,
                                        exit_mass, coverage, ws_e, st);
+        mark(1);
         if (e == hipSuccess)
             e = launch_tree_attn(q, k, v, dtype, parents, R, B, Hq, Hkv, D, P, scale, attn_out, ws_a, st);
+        mark(2);
         if (e == hipSuccess)
             e = launch_sample(logits, dtype, vec, parents, tokens, R, B, V, sL, ws_e, uniforms,
                               n_draws, exit_node, bonus_token, st);
+        mark(3);
         return e;
     }
 

@@ -25,7 +25,8 @@
 // k_attn_combine.
 //
 // k_attn_alu (fp32): one wave per query row, lanes over head_dim, online
-// softmax in fp32 -- a plain vector-ALU kernel for fp32 inputs.
+// softmax in fp32 over blocks of keys -- a plain vector-ALU kernel for fp32
+// inputs.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -39,6 +40,10 @@ namespace {
 
 // ----------------------------------------------------------------------------
 // fp32 vector-ALU kernel: grid (ceil(B*Hq/4), R), 256 threads, wave = one row.
+// Keys are taken in blocks of ALU_KB (the prefix rows, then the root path of
+// node i walked upward through the parents in LDS): the K and V loads of a
+// block are issued together (64 values per lane: 32 keys at head_dim 64, 16
+// at 128), then the block's scores update the online softmax at once.
 // ----------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_alu(const float *__restrict__ q,
@@ -49,6 +54,7 @@ __global__ __launch_bounds__(256) void k_attn_alu(const float *__restrict__ q,
                                                   float *__restrict__ out,
                                                   unsigned *__restrict__ status) {
     constexpr int PER = D / 64;
+    constexpr int ALU_KB = 32 / PER;   // keys per block
     const int r = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     __shared__ int s_par[256];
@@ -73,28 +79,55 @@ __global__ __launch_bounds__(256) void k_attn_alu(const float *__restrict__ q,
 #pragma unroll
     for (int p = 0; p < PER; p++) { qv[p] = qp[lane + 64 * p]; acc[p] = 0.f; }
     float m = -kInf, l = 0.f;
-    // prefix rows, then the root path of node i (walked upward)
-    int j = i;
-    for (int key = 0;; key++) {
-        int row;
-        if (key < P) {
-            row = key;
-        } else {
-            if (j < 0) break;
-            row = P + j;
-            j = s_par[j];
+    int j = i;   // next node of the root path (walked upward), -1 when done
+    for (int t0 = 0;; t0 += ALU_KB) {
+        int rows[ALU_KB];
+#pragma unroll
+        for (int u = 0; u < ALU_KB; u++) {
+            const int t = t0 + u;
+            if (t < P) {
+                rows[u] = t;
+            } else if (j >= 0) {
+                rows[u] = P + j;
+                j = s_par[j];
+            } else {
+                rows[u] = -1;
+            }
         }
-        float dot = 0.f;
+        if (rows[0] < 0) break;
+        float kx[ALU_KB][PER], vx[ALU_KB][PER];
 #pragma unroll
-        for (int p = 0; p < PER; p++) dot = fmaf(qv[p], kb[(size_t)row * D + lane + 64 * p], dot);
-        const float s = wave_sum_f(dot) * scale;
-        const float mn = fmaxf(m, s);
+        for (int u = 0; u < ALU_KB; u++)
+#pragma unroll
+            for (int p = 0; p < PER; p++) {
+                const size_t off = (size_t)max(rows[u], 0) * D + lane + 64 * p;
+                kx[u][p] = kb[off];
+                vx[u][p] = vb[off];
+            }
+        float sc[ALU_KB];
+        float bm = -kInf;
+#pragma unroll
+        for (int u = 0; u < ALU_KB; u++) {
+            float dot = 0.f;
+#pragma unroll
+            for (int p = 0; p < PER; p++) dot = fmaf(qv[p], kx[u][p], dot);
+            sc[u] = rows[u] >= 0 ? wave_sum_f(dot) * scale : -kInf;
+            bm = fmaxf(bm, sc[u]);
+        }
+        const float mn = fmaxf(m, bm);
         const float alpha = expf(m - mn);
-        const float pr = expf(s - mn);
-        l = l * alpha + pr;
+        l *= alpha;
 #pragma unroll
-        for (int p = 0; p < PER; p++) acc[p] = acc[p] * alpha + pr * vb[(size_t)row * D + lane + 64 * p];
+        for (int p = 0; p < PER; p++) acc[p] *= alpha;
+#pragma unroll
+        for (int u = 0; u < ALU_KB; u++) {
+            const float pr = rows[u] >= 0 ? expf(sc[u] - mn) : 0.f;
+            l += pr;
+#pragma unroll
+            for (int p = 0; p < PER; p++) acc[p] = fmaf(pr, vx[u][p], acc[p]);
+        }
         m = mn;
+        if (rows[ALU_KB - 1] < 0) break;
     }
 #pragma unroll
     for (int p = 0; p < PER; p++) o[lane + 64 * p] = acc[p] / l;

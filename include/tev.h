@@ -233,7 +233,8 @@ tev_status tev_verify_round_noalloc(const void *q, const void *k, const void *v,
 /* tev_verify_round, and for profiling: events[0..3] (hipEvent_t, created by
  * the caller, any entry may be NULL) are recorded on `stream` before the
  * vocabulary pass, after it, after the attention launch and after the last
- * launch, so that the caller can time each launch.  events may be NULL. */
+ * launch (fp32: before the exit law, after it, after the attention, after the
+ * draws), so that the caller can time each launch.  events may be NULL. */
 tev_status tev_verify_round_timed(const void *q, const void *k, const void *v,
                                   const void *logits, int dtype, const int32_t *parents,
                                   const int32_t *tokens, int R, int B, int V, int Hq, int Hkv,
