@@ -86,12 +86,42 @@ struct ExitPtrs {
 // ----------------------------------------------------------------------------
 // k_reach.
 // ----------------------------------------------------------------------------
-constexpr int ROW_BATCH = 4;        // rows per wave whose partials are loaded together
-constexpr int FAST_NC = 64;         // chunks per row held in registers (one per lane)
+constexpr int ROW_BATCH = 4;        // rows per wave in one pass (one per 16-lane DPP row)
+constexpr int SEG_CHUNKS = 4;       // consecutive chunks of a row per lane
+constexpr int FAST_NC = 16 * SEG_CHUNKS;   // chunks per row held in registers (16 lanes x 4)
 
-// Batches of rows a workgroup of nth threads needs for B rows.
+// Passes of rows a workgroup of nth threads needs for B rows.
 __host__ __device__ constexpr int reach_batches(int B, int nth) {
     return (B + (nth / 64) * ROW_BATCH - 1) / ((nth / 64) * ROW_BATCH);
+}
+
+// Reductions and scans within each 16-lane DPP row (four independent rows
+// per wave); every lane of a row receives the row's result.
+__device__ __forceinline__ float row16_max_f32(float x) {
+    x = fmaxf(x, wave::dpp_f<wave::kQuadXor1>(x));
+    x = fmaxf(x, wave::dpp_f<wave::kQuadXor2>(x));
+    x = fmaxf(x, wave::dpp_f<wave::kRowHalfMirror>(x));
+    return fmaxf(x, wave::dpp_f<wave::kRowMirror>(x));
+}
+__device__ __forceinline__ unsigned row16_or_u32(unsigned x) {
+    int y = (int)x;
+    y |= wave::dpp_i<wave::kQuadXor1>(y);
+    y |= wave::dpp_i<wave::kQuadXor2>(y);
+    y |= wave::dpp_i<wave::kRowHalfMirror>(y);
+    return (unsigned)(y | wave::dpp_i<wave::kRowMirror>(y));
+}
+__device__ __forceinline__ double row16_sum_f64(double x) {
+    x += wave::dpp_d<wave::kQuadXor1>(x);
+    x += wave::dpp_d<wave::kQuadXor2>(x);
+    x += wave::dpp_d<wave::kRowHalfMirror>(x);
+    return x + wave::dpp_d<wave::kRowMirror>(x);
+}
+// inclusive scan over the 16 lanes of each row, in lane order
+__device__ __forceinline__ double row16_incl_scan_f64(double x) {
+    x += wave::shr_d<1>(x);
+    x += wave::shr_d<2>(x);
+    x += wave::shr_d<4>(x);
+    return x + wave::shr_d<8>(x);
 }
 
 // Arguments of the reach for one launch.
@@ -144,20 +174,26 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
     const int pa = parents[rb0 + ti];
     const int tk = tokens[rb0 + ti];
     const float2 ct = W.cterm[rb0 + ti];
-    float pm[2][ROW_BATCH];
-    unsigned pf[2][ROW_BATCH];
-    double pr[2][ROW_BATCH], pcs[2][ROW_BATCH];
-    // Loads the partials of batch BT (rows wave + REACH_WAVES * (ROW_BATCH * BT + q)) into buffer BUF.
+    // Row pass layout: each 16-lane DPP row of a wave takes one tree row per
+    // pass, lane sl holding the row's chunks 4 sl .. 4 sl + 3 (nc <= 64), so a
+    // wave combines four rows at once with in-row DPP steps only.
+    const int sl = lane & 15;
+    const int rrow = wave * ROW_BATCH + (lane >> 4);   // row of this lane within a pass
+    float pm[2][SEG_CHUNKS];
+    unsigned pf[2][SEG_CHUNKS];
+    double pr[2][SEG_CHUNKS], pcs[2][SEG_CHUNKS];
+    // Loads the partials of pass BT (row BT * ROW_BATCH * REACH_WAVES + rrow) into buffer BUF.
 #define TEV_REACH_LOAD(BUF, BT)                                                                 \
     {                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
-            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
-            const bool ok = v < B && lane < nc;   /* masked where used; unused when !fast */   \
-            const size_t o = (rb0 + (ok ? v : 0)) * nc + (ok ? lane : 0);                       \
-            pm[BUF][q] = W.part_m[o];                                                           \
-            pf[BUF][q] = W.flags[o];                                                            \
-            pr[BUF][q] = W.part_r[o];                                                           \
-            pcs[BUF][q] = W.part_c[o];                                                          \
+        const int v = (BT) * ROW_BATCH * REACH_WAVES + rrow;                                    \
+        _Pragma("unroll") for (int j = 0; j < SEG_CHUNKS; j++) {                                \
+            const int c = SEG_CHUNKS * sl + j;                                                  \
+            const bool ok = v < B && c < nc;   /* masked where used; unused when !fast */       \
+            const size_t o = (rb0 + (ok ? v : 0)) * nc + (ok ? c : 0);                          \
+            pm[BUF][j] = W.part_m[o];                                                           \
+            pf[BUF][j] = W.flags[o];                                                            \
+            pr[BUF][j] = W.part_r[o];                                                           \
+            pcs[BUF][j] = W.part_c[o];                                                          \
         }                                                                                       \
     }
     TEV_REACH_LOAD(0, 0)
@@ -174,35 +210,52 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
     // chunk offsets are integers, so rescaling a partial to the row offset M
     // is an exact power of two.
     auto finish_row = [&](int v, float M, unsigned f, double carry, double csum) {
-        csum = wave::sum_f64(csum);
         const double Z = carry + csum;
         if (!(M > -kInf) || !(Z > 0.0) || isnan(Z)) f |= TEV_FLAG_NONFINITE;
-        if (lane == 0) {
-            s_M[v] = M;
-            s_Z[v] = Z;
-            s_rho[v] = carry / Z;
-            W.row_m[rb0 + v] = M;
-            if (f) atomicOr(&s_flags, f);
-        }
+        s_M[v] = M;
+        s_Z[v] = Z;
+        s_rho[v] = carry / Z;
+        W.row_m[rb0 + v] = M;
+        if (f) atomicOr(&s_flags, f);
     };
     if (fast) {
+        // Per row: the offset M (row maximum of the chunk offsets), the flags,
+        // the running residual sums in chunk order (a serial prefix over the
+        // lane's four chunks, then a scan over the row's lanes) and the
+        // child-sum total; lane 15 of the row holds the residual total.
 #define TEV_REACH_ROWS(BUF, BT)                                                                 \
     {                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < ROW_BATCH; q++) {                                 \
-            const int v = wave + REACH_WAVES * (ROW_BATCH * (BT) + q);                           \
-            if (v < B) {                                                                        \
-                const bool ok = lane < nc;                                                      \
-                const float mc = ok ? pm[BUF][q] : -kInf;                                       \
-                const float M = wave::max_f32(mc);                                              \
-                const unsigned f = wave::or_u32(ok ? pf[BUF][q] : 0u);                          \
-                const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;                        \
-                const double incl = wave::incl_scan_f64(ok ? pr[BUF][q] * sc : 0.0, lane);      \
-                if (ok) W.rcum[(rb0 + v) * nc + lane] = incl;                                   \
-                finish_row(v, M, f, wave::last_lane_d(incl), ok ? pcs[BUF][q] * sc : 0.0);      \
+        const int v = (BT) * ROW_BATCH * REACH_WAVES + rrow;                                    \
+        float mloc = -kInf;                                                                     \
+        unsigned floc = 0u;                                                                     \
+        _Pragma("unroll") for (int j = 0; j < SEG_CHUNKS; j++) {                                \
+            const bool ok = SEG_CHUNKS * sl + j < nc;                                           \
+            mloc = fmaxf(mloc, ok ? pm[BUF][j] : -kInf);                                        \
+            floc |= ok ? pf[BUF][j] : 0u;                                                       \
+        }                                                                                       \
+        const float M = row16_max_f32(mloc);                                                    \
+        const unsigned f = row16_or_u32(floc);                                                  \
+        double pre[SEG_CHUNKS], cs = 0.0, run = 0.0;                                            \
+        _Pragma("unroll") for (int j = 0; j < SEG_CHUNKS; j++) {                                \
+            const bool ok = SEG_CHUNKS * sl + j < nc;                                           \
+            const float mc = ok ? pm[BUF][j] : -kInf;                                           \
+            const double sc = (mc > -kInf) ? pow2_int(mc - M) : 0.0;                            \
+            run += ok ? pr[BUF][j] * sc : 0.0;                                                  \
+            pre[j] = run;                                                                       \
+            cs += ok ? pcs[BUF][j] * sc : 0.0;                                                  \
+        }                                                                                       \
+        const double incl = row16_incl_scan_f64(run);                                           \
+        const double excl = wave::shr_d<1>(incl);                                               \
+        const double csum = row16_sum_f64(cs);                                                  \
+        if (v < B) {                                                                            \
+            _Pragma("unroll") for (int j = 0; j < SEG_CHUNKS; j++) {                            \
+                const int c = SEG_CHUNKS * sl + j;                                              \
+                if (c < nc) W.rcum[(rb0 + v) * nc + c] = excl + pre[j];                         \
             }                                                                                   \
+            if (sl == 15) finish_row(v, M, f, incl, csum);                                      \
         }                                                                                       \
     }
-        // batch bt + 1 is issued before batch bt's stores
+        // pass bt + 1 is issued before pass bt's stores
 #pragma unroll
         for (int bt = 0; bt < NB; bt++) {
             if (bt + 1 < NB) TEV_REACH_LOAD((bt + 1) & 1, bt + 1)
@@ -234,7 +287,8 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
                 if (cc < nc) W.rcum[base + cc] = carry + incl;
                 carry += wave::last_lane_d(incl);
             }
-            finish_row(v, M, f, carry, csum);
+            csum = wave::sum_f64(csum);
+            if (lane == 0) finish_row(v, M, f, carry, csum);
         }
     }
 #undef TEV_REACH_LOAD

@@ -15,6 +15,8 @@ pytestmark = pytest.mark.gpu
 SMALL = [
     dict(name="bf16_d128_ragged", R=2, B=37, Hq=8, Hkv=2, D=128, P=300, tree="random"),
     dict(name="bf16_d64", R=1, B=50, Hq=6, Hkv=3, D=64, P=517, tree="random"),
+    dict(name="bf16_d64_few_rows", R=2, B=21, Hq=2, Hkv=2, D=64, P=333, tree="random"),
+    dict(name="bf16_d64_wide", R=1, B=200, Hq=4, Hkv=2, D=64, P=1100, tree="random"),
     dict(name="bf16_g1", R=1, B=33, Hq=2, Hkv=2, D=128, P=96, tree="random"),
     dict(name="bf16_no_prefix", R=1, B=40, Hq=4, Hkv=1, D=128, P=0, tree="random"),
     dict(name="bf16_root_only", R=3, B=1, Hq=4, Hkv=2, D=128, P=200, tree="random"),
