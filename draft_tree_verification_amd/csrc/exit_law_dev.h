@@ -304,9 +304,11 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
         s_prod[tid] = pc;
     }
     __syncthreads();
-    if (wave != 0) return;
 
     // ---- tree pass (wave 0): lane owns nodes NPL*lane .. NPL*lane + NPL - 1 ----
+    // (the other waves return at once; a caller that runs more work in this
+    // workgroup synchronises after it)
+    auto tree_pass = [&]() {
     if (fl) {
         const float qnan = __builtin_nanf("");
 #pragma unroll
@@ -399,6 +401,8 @@ __device__ __forceinline__ void reach_wg(const ReachArgs &A, const int r) {
         cov_out[r] = (float)C;
         W.status[r] = 0u;
     }
+    };
+    if (wave == 0) tree_pass();
 }
 
 // ----------------------------------------------------------------------------
@@ -548,27 +552,32 @@ struct SampleArgs {
     int32_t *exit_node, *bonus_token;
 };
 
-// Sum of one int per thread over a 256-thread workgroup (every thread gets
-// it); red is a 4-entry LDS scratch, reused only after a barrier.
+// Sum of one int per thread over an NTH-thread workgroup (every thread gets
+// it); red is an NTH / 64-entry LDS scratch, reused only after a barrier.
+template <int NTH>
 __device__ __forceinline__ int block_sum_i32(int x, int *red) {
     const int w = wave::sum_i32(x);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
     __syncthreads();
-    const int t = (red[0] + red[1]) + (red[2] + red[3]);
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < NTH / 64; i++) t += red[i];
     __syncthreads();
     return t;
 }
 
-// Draw n of request r by one 256-thread workgroup (4 waves).  Loads come in
+// Draw n of request r by one workgroup of NTH >= 256 threads.  Loads come in
 // three dependent rounds, each issued as one group of unconditional loads:
 // (1) everything that does not depend on the draw, (2) the exit node's running
-// residual sums, (3) the one chunk that holds the bonus token, which the four
-// waves scan together (thread t owns tokens [16 t, 16 t + 16) of it).
+// residual sums, (3) the one chunk that holds the bonus token, which the first
+// four waves scan together (thread t owns tokens [16 t, 16 t + 16) of it; the
+// other waves only join the barriers), so the draw is the same for any NTH.
 constexpr int SAMPLE_THREADS = 256;
 constexpr int SPT = CHUNK / SAMPLE_THREADS;   // 16 tokens per thread
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int NTH = SAMPLE_THREADS>
 __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, const int r) {
+    static_assert(NTH >= SAMPLE_THREADS && NTH % 64 == 0, "at least four waves");
     const T *__restrict__ logits = A.logits;
     const int32_t *__restrict__ parents = A.parents;
     const int32_t *__restrict__ tokens = A.tokens;
@@ -579,8 +588,9 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
     const double *__restrict__ wcum = A.wcum;
     const int n_draws = A.n_draws;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ int s_red[4];
-    __shared__ double s_wsum[4];
+    const bool act = tid < SAMPLE_THREADS;   // scans the chunk
+    __shared__ int s_red[NTH / 64];
+    __shared__ double s_wsum[NTH / 64];
     __shared__ unsigned s_bits[SAMPLE_THREADS];
     const size_t kd = (size_t)r * n_draws + n;
 
@@ -600,7 +610,7 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
     }
     // Exit node: the number of j with W_j <= u1 * S is the smallest j with u1 S < W_j.
     const double t1 = u1 * Wtot;
-    int Vn = block_sum_i32((tid < B && wj <= t1) ? 1 : 0, s_red);
+    int Vn = block_sum_i32<NTH>((tid < B && wj <= t1) ? 1 : 0, s_red);
     if (Vn >= B) {   // rounding left no bin: last node with positive mass
         int best = -1;
         for (int j = lane; j < B; j += 64)
@@ -613,12 +623,12 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
     const double *RC = rcum + rb * nc;
     const double t2 = u2 * RC[nc - 1];
     int ccount = 0;
-    for (int c0 = 0; c0 < nc; c0 += SAMPLE_THREADS) {
+    for (int c0 = 0; c0 < nc; c0 += NTH) {
         const int c = c0 + tid;
         const double rc = RC[min(c, nc - 1)];
         ccount += (c < nc && rc <= t2) ? 1 : 0;
     }
-    int cc = block_sum_i32(ccount, s_red);
+    int cc = block_sum_i32<NTH>(ccount, s_red);
     if (cc >= nc) {
         int best = -1;
         for (int c = lane; c < nc; c += 64)
@@ -657,14 +667,14 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
     const double target = __builtin_ldexp(t2 - before, (int)fminf(Mv - Mc, 2000.f));
 
     // child tokens of Vn inside the chunk: bit j of word t marks token 16 t + j
-    s_bits[tid] = 0u;
+    if (act) s_bits[tid] = 0u;
     __syncthreads();
     {
         const int o = ctok - c0;
         if ((1 + tid < B) & (cpar == Vn) & (o >= 0) & (o < len)) atomicOr(&s_bits[o / SPT], 1u << (o % SPT));
     }
     __syncthreads();
-    const unsigned bits = s_bits[tid];
+    const unsigned bits = act ? s_bits[tid] : 0u;
     const float off = (Mc > -kInf) ? Mc : 0.f;   // a chunk of -inf logits has only zero terms
     float e[SPT];
     double seg = 0.0;
@@ -685,15 +695,18 @@ __device__ __forceinline__ void sample_wg(const SampleArgs<T> &A, const int n, c
 #pragma unroll
     for (int j = 0; j < SPT; j++) {
         run += (double)e[j];
-        below += (run <= target) ? 1 : 0;
+        below += (act && run <= target) ? 1 : 0;
         if (e[j] > 0.f) last_pos = tid * SPT + j;
     }
-    below = block_sum_i32(below, s_red);
+    below = block_sum_i32<NTH>(below, s_red);
     if (below >= len) {
         const int lp = wave::max_i32(last_pos);
         if (lane == 0) s_red[wave] = lp;
         __syncthreads();
-        below = max(max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])), 0);
+        int m = -1;
+#pragma unroll
+        for (int i = 0; i < NTH / 64; i++) m = max(m, s_red[i]);
+        below = max(m, 0);
     }
     if (tid == 0) {
         A.exit_node[kd] = Vn;

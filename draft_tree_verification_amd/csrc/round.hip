@@ -11,9 +11,12 @@
 //   1. k_vocab                       -- the logit stream (all CUs);
 //   2. k_round_attn = attention workgroups + one reach workgroup per request:
 //      the attention plan leaves that many CUs free, and the reach needs only
-//      the vocabulary pass, finished by the stream order;
-//   3. k_round_tail = draw workgroups + the split combine of the attention:
-//      the draws need the reach, the combine the attention, both done.
+//      the vocabulary pass, finished by the stream order.  With at most
+//      DRAWS_IN_REACH draws per request the reach workgroup also makes them,
+//      right after the exit CDF (the same arithmetic as a draw workgroup);
+//   3. k_round_tail = the split combine of the attention, and the draw
+//      workgroups when there are more draws (they need the reach, the
+//      combine the attention, both done).  No launch when neither is left.
 //
 // Workgroups of one launch never wait for each other, so no cross-workgroup
 // synchronisation is involved; the roles only share the launch.
@@ -30,11 +33,22 @@ namespace {
 
 // Launch 2: workgroups [0, attn_grid) are attention tasks, the next R are the
 // reach of request b - attn_grid (512 threads, NB batches of rows).
+constexpr int DRAWS_IN_REACH = 4;
+
 template <int D, int NQT, int NB>
-__global__ __launch_bounds__(NT) void k_round_attn(AttnArgs a, ReachArgs ra, int attn_grid) {
+__global__ __launch_bounds__(NT) void k_round_attn(AttnArgs a, ReachArgs ra, int attn_grid,
+                                                   SampleArgs<uint16_t> sa, int reach_draws, int vec) {
     const int b = (int)blockIdx.x;
     if (b >= attn_grid) {
-        reach_wg<NB, NT>(ra, b - attn_grid);
+        const int r = b - attn_grid;
+        reach_wg<NB, NT>(ra, r);
+        if (reach_draws) {
+            __syncthreads();   // the exit CDF, residual sums and status of request r
+            for (int n = 0; n < sa.n_draws; n++) {
+                if (vec) sample_wg<uint16_t, true, NT>(sa, n, r);
+                else sample_wg<uint16_t, false, NT>(sa, n, r);
+            }
+        }
         return;
     }
     const int task = xcd_task(b, a.n_wg);
@@ -65,34 +79,46 @@ __global__ __launch_bounds__(VOCAB_THREADS) void k_round_tail(SampleArgs<T> sa, 
                        ca.status, ca.out, b - n_sample);
 }
 
+struct RoundDraws {
+    SampleArgs<uint16_t> sa;
+    int in_reach, vec;
+};
+
 template <int D, int NQT, int NB>
-void launch_round_attn(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R, hipStream_t st) {
-    k_round_attn<D, NQT, NB><<<dim3((unsigned)(attn_grid + R)), NT, 0, st>>>(a, ra, attn_grid);
+void launch_round_attn(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R,
+                       const RoundDraws &rd, hipStream_t st) {
+    k_round_attn<D, NQT, NB><<<dim3((unsigned)(attn_grid + R)), NT, 0, st>>>(a, ra, attn_grid, rd.sa,
+                                                                             rd.in_reach, rd.vec);
 }
 
 template <int D, int NQT>
-void round_attn_nb(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R, int B, hipStream_t st) {
+void round_attn_nb(const AttnArgs &a, const ReachArgs &ra, int attn_grid, int R, int B,
+                   const RoundDraws &rd, hipStream_t st) {
     const int nb = reach_batches(B, NT);
-    if (nb <= 2) launch_round_attn<D, NQT, 2>(a, ra, attn_grid, R, st);
-    else if (nb <= 4) launch_round_attn<D, NQT, 4>(a, ra, attn_grid, R, st);
-    else launch_round_attn<D, NQT, 8>(a, ra, attn_grid, R, st);
+    if (nb <= 2) launch_round_attn<D, NQT, 2>(a, ra, attn_grid, R, rd, st);
+    else if (nb <= 4) launch_round_attn<D, NQT, 4>(a, ra, attn_grid, R, rd, st);
+    else launch_round_attn<D, NQT, 8>(a, ra, attn_grid, R, rd, st);
 }
 
+// n_draws draw workgroups per request, then the combine workgroups of the
+// split partials (none without splits; no launch when neither is left).
 template <int D, typename T, bool VEC>
 void launch_round_tail(const SampleArgs<T> &sa, int R, int n_draws, const CombineArgs &ca,
-                       int n_combine, hipStream_t st) {
+                       hipStream_t st) {
     static_assert(SAMPLE_THREADS == VOCAB_THREADS, "draw and combine workgroups share a launch");
+    const int n_combine = ca.splits > 1 ? (int)((ca.rows_all + 3) / 4) : 0;
     const int sbx = n_draws;
     const int n_sample = R * sbx;
+    if (n_sample + n_combine == 0) return;
     k_round_tail<D, T, VEC><<<dim3((unsigned)(n_sample + n_combine)), VOCAB_THREADS, 0, st>>>(
         sa, sbx, n_sample, ca);
 }
 
 template <int D, typename T>
 void round_tail_vec(bool vec, const SampleArgs<T> &sa, int R, int n_draws, const CombineArgs &ca,
-                    int n_combine, hipStream_t st) {
-    if (vec) launch_round_tail<D, T, true>(sa, R, n_draws, ca, n_combine, st);
-    else launch_round_tail<D, T, false>(sa, R, n_draws, ca, n_combine, st);
+                    hipStream_t st) {
+    if (vec) launch_round_tail<D, T, true>(sa, R, n_draws, ca, st);
+    else launch_round_tail<D, T, false>(sa, R, n_draws, ca, st);
 }
 
 }  // namespace
@@ -148,23 +174,24 @@ hipError_t launch_round(const void *q, const void *k, const void *v, const void 
                      part_ml, astatus};
     const ReachArgs ra{parents, tokens, B, V, n_chunks(V), sL, exit_ptrs(ws_e, R, B, V), rho, reach,
                        exit_mass, coverage};
-    if (D == 64 && pl.nqt == 1) round_attn_nb<64, 1>(a, ra, attn_grid, R, B, st);
-    else if (D == 64) round_attn_nb<64, 2>(a, ra, attn_grid, R, B, st);
-    else if (pl.nqt == 1) round_attn_nb<128, 1>(a, ra, attn_grid, R, B, st);
-    else round_attn_nb<128, 2>(a, ra, attn_grid, R, B, st);
+    const SampleArgs<uint16_t> sa = sample_args((const uint16_t *)logits, parents, tokens, R, B, V, sL,
+                                                ws_e, uniforms, n_draws, exit_node, bonus_token);
+    const RoundDraws rd{sa, n_draws <= DRAWS_IN_REACH ? 1 : 0, vec ? 1 : 0};
+    if (D == 64 && pl.nqt == 1) round_attn_nb<64, 1>(a, ra, attn_grid, R, B, rd, st);
+    else if (D == 64) round_attn_nb<64, 2>(a, ra, attn_grid, R, B, rd, st);
+    else if (pl.nqt == 1) round_attn_nb<128, 1>(a, ra, attn_grid, R, B, rd, st);
+    else round_attn_nb<128, 2>(a, ra, attn_grid, R, B, rd, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     mark(2);
 
-    // 3. draws + split combine
+    // 3. split combine, and the draws left to a launch of their own
     const int G = Hq / Hkv;
     const size_t rows_all = (size_t)R * Hkv * G * B;
     const CombineArgs ca{part_o, part_ml, pl.splits, Hkv, G, B, Hq, rows_all, astatus, attn_out};
-    const int n_combine = pl.splits > 1 ? (int)((rows_all + 3) / 4) : 0;
-    const SampleArgs<uint16_t> sa = sample_args((const uint16_t *)logits, parents, tokens, R, B, V, sL,
-                                                ws_e, uniforms, n_draws, exit_node, bonus_token);
-    if (D == 64) round_tail_vec<64, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
-    else round_tail_vec<128, uint16_t>(vec, sa, R, n_draws, ca, n_combine, st);
+    const int tail_draws = rd.in_reach ? 0 : n_draws;
+    if (D == 64) round_tail_vec<64, uint16_t>(vec, sa, R, tail_draws, ca, st);
+    else round_tail_vec<128, uint16_t>(vec, sa, R, tail_draws, ca, st);
     e = hipGetLastError();
     mark(3);
     return e;

@@ -128,6 +128,40 @@ def test_round_named(name):
     GP.log(f"[round] {name} ok: {len(err)} attention rows, max row error {err.max():.3e}")
 
 
+DRAW_CASES = [c["name"] for c in SMALL if c.get("dtype", "bf16") == "bf16"] + \
+    [n for n in NAMED if n != "tiny"]
+
+
+@pytest.mark.parametrize("name", DRAW_CASES)
+@pytest.mark.parametrize("n_draws", [1, 4])
+def test_round_draws_in_reach(name, n_draws):
+    """With at most four draws per request the round makes them in the reach
+    workgroup beside the attention: exit nodes and bonus tokens bit-equal to
+    tev_sample after tev_exit_law on the same inputs, and equal to the
+    oracle's outside the 1e-6 band."""
+    small = {c["name"]: c for c in SMALL}
+    if name in small:
+        c = dict(small[name])
+        c.pop("name")
+        wl = W.make_custom(name, dtype=c.pop("dtype", "bf16"), n_uniform=n_draws, **c)
+    else:
+        wl = W.make_config(name, n_uniform=n_draws)
+    GP.log(f"[round] draws in the reach workgroup: {name}, {n_draws} per request")
+    res, flags, (lg, par, tok, uni) = _run_round(wl)
+    assert np.all(flags == 0), flags
+    el = tev.tev_exit_law(lg, par, tok, wl.inv_temperature)
+    en, bt = tev.tev_sample(lg, par, tok, el.workspace, uni, wl.inv_temperature)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(res.exit_node.cpu().numpy(), en.cpu().numpy(), err_msg="exit_node")
+    np.testing.assert_array_equal(res.bonus_token.cpu().numpy(), bt.cpu().numpy(), err_msg="bonus_token")
+    ora = oracle.exit_law(wl.logits, wl.dtype, wl.parents, wl.tokens, wl.inv_temperature)
+    dr = oracle.sample(wl.logits, wl.dtype, wl.parents, wl.tokens, ora.exit_mass, wl.uniforms,
+                       wl.inv_temperature)
+    ok = ~(dr.band_exit | dr.band_bonus)
+    assert np.array_equal(res.exit_node.cpu().numpy()[ok], dr.exit_node[ok])
+    assert np.array_equal(res.bonus_token.cpu().numpy()[ok], dr.bonus_token[ok])
+
+
 def test_round_invalid_tree_is_flagged():
     wl = W.make_custom("round_bad", R=2, B=12, V=9000, dtype="bf16", tree="random", Hq=4, Hkv=2,
                        D=128, P=64, n_uniform=16)
