@@ -985,9 +985,11 @@ def main():
                         **vocab_roof(phase_us["k_vocab"])),
         "k_round_attn": dict(us=round(phase_us["k_round_attn"], 3), bytes=work["attn_bytes"],
                              flops=work["attn_flops"], **attn_roof(phase_us["k_round_attn"]),
-                             note="attention workgroups + the reach workgroup of each request"),
+                             note="attention workgroups + the reach workgroup of each request, which also "
+                                  "makes the request's draws (at most four per request)"),
         "k_round_tail": {"us": round(phase_us["k_round_tail"], 3),
-                         "note": "draw workgroups + the attention split combine"},
+                         "note": "the attention split combine (no launch without prefix splits); draw "
+                                 "workgroups only with more than four draws per request"},
         "separate_calls_us": {k: round(v, 3) for k, v in per_call.items()},
         "verifier_decision_us": {"tev_sample (exit node + bonus)": round(per_call["tev_sample"], 3),
                                  "tev_predraw (B node draws + walk)": round(per_call["tev_predraw"], 3),
