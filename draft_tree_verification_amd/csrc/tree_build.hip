@@ -395,11 +395,21 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
         }
         const double ws = wave::readlane_d(mine.s, wl);
         const double wsz = wave::readlane_d(mine.sz, wl);
+        const double wpsz = wave::readlane_d(mine.psz, wl);
+        const float wzn = wave::readlane_f(mine.zn, wl);
         const uint64_t whi = readlane_u64(mine.hi, wl), wlo = readlane_u64(mine.lo, wl);
         const int d = __builtin_amdgcn_readlane(mine.depth, wl);
         const int wq = __builtin_amdgcn_readlane(bq, wl);
         const int rk = rank_at(whi, wlo, d);
         const int parent = wq * 64 + wl;                 // the slot's node
+        // Everything the two new slots need, as uniform values read at once:
+        // the constants of depths d and d + 1 (lanes 1..L; the child exists
+        // only for d < L) and the logit after the next sibling (LDS
+        // broadcast, clamped index).
+        const int d1 = min(d + 1, L);
+        const double cd = wave::readlane_d(creg, d), cd1 = wave::readlane_d(creg, d1);
+        const float z0 = wave::readlane_f(zr0, d1), z1 = wave::readlane_f(zr1, d1);
+        const float zn2 = s_tz[(d - 1) * K + min(rk + 2, K - 1)];
         if (lane == 0) {
             s_par[n] = parent;
             s_idx[n] = (d - 1) * K + rk;
@@ -407,33 +417,34 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
             s_hi[n] = whi;
             s_lo[n] = wlo;
         }
-        // the winner's slot moves on to the next sibling (or empties)
+        // the winner's slot moves on to the next sibling (or empties) ...
+        Slot sib{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
+        if (rk + 1 < K) {
+            sib.psz = wpsz;
+            sib.sz = wpsz + (double)wzn;
+            sib.s = (sib.sz - cd) + lp;
+            sib.hi = whi;
+            sib.lo = wlo;
+            set_rank(sib.hi, sib.lo, d, rk + 1);
+            sib.zn = rk + 2 < K ? zn2 : qnan;
+            sib.depth = d;
+        }
+        // ... and node n's slot starts with its rank-0 child (both computed
+        // by every lane, then moved into their owners' registers)
+        Slot ch;
+        ch.psz = wsz;
+        ch.sz = wsz + (double)z0;
+        ch.s = (ch.sz - cd1) + lp;
+        ch.hi = whi;                                      // rank 0 at depth d + 1: byte already 0
+        ch.lo = wlo;
+        ch.zn = z1;
+        ch.depth = d + 1;
         if (lane == wl) {
-            Slot sib{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
-            if (rk + 1 < K) {
-                sib.psz = mine.psz;
-                sib.sz = mine.psz + (double)mine.zn;
-                sib.s = (sib.sz - wave::readlane_d(creg, d)) + lp;
-                sib.hi = whi;
-                sib.lo = wlo;
-                set_rank(sib.hi, sib.lo, d, rk + 1);
-                sib.zn = rk + 2 < K ? s_tz[(d - 1) * K + rk + 2] : qnan;
-                sib.depth = d;
-            }
 #pragma unroll
             for (int q = 0; q < SLOTS; q++)
                 if (q == wq) f[q] = sib;                 // wq is uniform: one branch taken
         }
-        // node n's slot starts with its rank-0 child
         if (d < L && lane == (n & 63)) {
-            Slot ch;
-            ch.psz = wsz;
-            ch.sz = wsz + (double)wave::readlane_f(zr0, d + 1);
-            ch.s = (ch.sz - wave::readlane_d(creg, d + 1)) + lp;
-            ch.hi = whi;                                  // rank 0 at depth d + 1: byte already 0
-            ch.lo = wlo;
-            ch.zn = wave::readlane_f(zr1, d + 1);
-            ch.depth = d + 1;
 #pragma unroll
             for (int q = 0; q < SLOTS; q++)
                 if (q == (n >> 6)) f[q] = ch;
