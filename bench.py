@@ -285,6 +285,29 @@ def summarize_pmc(config: str, dbs):
     print(json.dumps(out, indent=1))
 
 
+def summarize_trace(db: str):
+    """Per-kernel durations of a rocprofv3 --kernel-trace database (the
+    kernels view: end - start of every dispatch), as the markdown table the
+    kernel-trace summaries under profiles/ hold: calls, total, average,
+    median and minimum in microseconds, and each kernel's share of the total."""
+    import sqlite3
+    import statistics
+    from collections import defaultdict
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    ki = cols.index("kernel_name") if "kernel_name" in cols else cols.index("name")
+    si, ei = cols.index("start"), cols.index("end")
+    dur = defaultdict(list)
+    for row in con.execute("select * from kernels"):
+        dur[row[ki]].append((row[ei] - row[si]) / 1000.0)
+    total = sum(sum(v) for v in dur.values())
+    print("| kernel | calls | total (us) | average (us) | median (us) | min (us) | share |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k[:70]}` | {len(v)} | {sum(v):.1f} | {sum(v) / len(v):.3f} | "
+              f"{statistics.median(v):.3f} | {min(v):.3f} | {100 * sum(v) / total:.1f}% |")
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -593,6 +616,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DB",
                     help="write profiles/pmc_<workload>.json from the rocprofv3 --pmc databases "
                          "(one per counter pass) of a --counters run")
+    ap.add_argument("--summarize-trace", metavar="DB",
+                    help="print the per-kernel duration table of a rocprofv3 --kernel-trace database")
     ap.add_argument("--separate", action="store_true",
                     help="time the three calls tev_tree_attn, tev_exit_law, tev_sample instead of tev_verify_round")
     ap.add_argument("--no-extra", action="store_true",
@@ -604,6 +629,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.config, args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
 
     if args.gpus != 1:
