@@ -590,10 +590,10 @@ constexpr int MAX_SPLITS = 32;
 
 // Merge split partials: one wave per query row (block b of 256 threads takes
 // rows 4b .. 4b + 3); lane s reads split s's (m, l, u), every lane its D/64
-// output columns of all splits.  All loads are unconditional (clamped split
-// index), so they are all in flight before the first use.
-template <int D>
-__device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ part_o,
+// output columns of NS >= splits splits.  All loads are unconditional
+// (clamped split index), so they are all in flight before the first use.
+template <int D, int NS>
+__device__ __forceinline__ void attn_combine_ns(const uint16_t *__restrict__ part_o,
                                                 const float *__restrict__ part_ml, int splits,
                                                 int Hkv, int G, int B, int Hq, size_t rows_all,
                                                 const unsigned *__restrict__ status,
@@ -609,9 +609,9 @@ __device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ par
     const int r = rg / Hkv, g = rg - r * Hkv;
     const int i = rr / G, hh = rr - i * G;
     const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + ((size_t)min(lane, splits - 1) * rows_all + row) * 4);
-    uint32_t o[MAX_SPLITS];   // DPL fp16 values of split s (one or two halves)
+    uint32_t o[NS];   // DPL fp16 values of split s (one or two halves)
 #pragma unroll
-    for (int s = 0; s < MAX_SPLITS; s++) {
+    for (int s = 0; s < NS; s++) {
         const uint16_t *p = part_o + ((size_t)min(s, splits - 1) * rows_all + row) * D + lane * DPL;
         o[s] = DPL == 2 ? *reinterpret_cast<const uint32_t *>(p) : (uint32_t)*p;
     }
@@ -625,7 +625,7 @@ __device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ par
 #pragma unroll
     for (int j = 0; j < DPL; j++) acc[j] = 0.f;
 #pragma unroll
-    for (int s = 0; s < MAX_SPLITS; s++) {
+    for (int s = 0; s < NS; s++) {
         if (s < splits) {
             const float fs = wave::readlane_f(f, s);
 #pragma unroll
@@ -639,6 +639,20 @@ __device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ par
     float *dst = out + (((size_t)r * B + i) * Hq + g * G + hh) * D + lane * DPL;
 #pragma unroll
     for (int j = 0; j < DPL; j++) dst[j] = bad ? __builtin_nanf("") : acc[j] / L;
+}
+
+// Loads as many splits as the launch can have: 16, or MAX_SPLITS (splits is
+// uniform, so one branch is taken; the loads of each stay unconditional).
+template <int D>
+__device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ part_o,
+                                                const float *__restrict__ part_ml, int splits,
+                                                int Hkv, int G, int B, int Hq, size_t rows_all,
+                                                const unsigned *__restrict__ status,
+                                                float *__restrict__ out, const int block) {
+    if (splits <= 16)
+        attn_combine_ns<D, 16>(part_o, part_ml, splits, Hkv, G, B, Hq, rows_all, status, out, block);
+    else
+        attn_combine_ns<D, MAX_SPLITS>(part_o, part_ml, splits, Hkv, G, B, Hq, rows_all, status, out, block);
 }
 
 }  // namespace

@@ -23,6 +23,9 @@ SMALL = [
     dict(name="bf16_chain_256", R=1, B=256, Hq=4, Hkv=2, D=128, P=64, tree="chain"),
     dict(name="bf16_star_256", R=1, B=256, Hq=2, Hkv=1, D=128, P=1000, tree="star"),
     dict(name="bf16_split_prefix", R=1, B=64, Hq=32, Hkv=8, D=128, P=2048, tree="best_first"),
+    # one kv head and a long prefix: 32 prefix splits (the combine path for more than 16)
+    dict(name="bf16_many_splits", R=1, B=20, Hq=4, Hkv=1, D=128, P=4096, tree="random"),
+    dict(name="bf16_d64_many_splits", R=2, B=9, Hq=2, Hkv=1, D=64, P=3000, tree="random"),
     dict(name="f32_d64", R=2, B=16, Hq=4, Hkv=4, D=64, P=128, tree="random", dtype="f32"),
     dict(name="f32_d128_gqa", R=1, B=23, Hq=6, Hkv=2, D=128, P=77, tree="random", dtype="f32"),
 ]
