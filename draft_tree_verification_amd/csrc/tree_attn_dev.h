@@ -641,7 +641,7 @@ __device__ __forceinline__ void attn_combine_ns(const uint16_t *__restrict__ par
     for (int j = 0; j < DPL; j++) dst[j] = bad ? __builtin_nanf("") : acc[j] / L;
 }
 
-// Loads as many splits as the launch can have: 16, or MAX_SPLITS (splits is
+// Loads as many splits as the launch can have: 8, 16, or MAX_SPLITS (splits is
 // uniform, so one branch is taken; the loads of each stay unconditional).
 template <int D>
 __device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ part_o,
@@ -649,7 +649,9 @@ __device__ __forceinline__ void attn_combine_wg(const uint16_t *__restrict__ par
                                                 int Hkv, int G, int B, int Hq, size_t rows_all,
                                                 const unsigned *__restrict__ status,
                                                 float *__restrict__ out, const int block) {
-    if (splits <= 16)
+    if (splits <= 8)
+        attn_combine_ns<D, 8>(part_o, part_ml, splits, Hkv, G, B, Hq, rows_all, status, out, block);
+    else if (splits <= 16)
         attn_combine_ns<D, 16>(part_o, part_ml, splits, Hkv, G, B, Hq, rows_all, status, out, block);
     else
         attn_combine_ns<D, MAX_SPLITS>(part_o, part_ml, splits, Hkv, G, B, Hq, rows_all, status, out, block);
