@@ -32,6 +32,8 @@
 //               winner's slot to the next sibling and opens the new node's
 //               slot with its rank-0 child.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -70,13 +72,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 // The K best of the keys the workgroup holds, N per thread (0 = no key),
 // written best first to out[0..K) (0 past the last key).  The K-th largest
 // per-thread maximum bounds the K-th key from below (K threads hold a key at
-// least that large), so only keys at or above it -- at most N K of them, from
-// those K threads -- are compacted into LDS, where each is ranked by counting
-// the larger ones.  Keys are unique, so the ranks are distinct.
+// least that large), and so does the caller's floor (0: none); only keys at or
+// above the larger bound -- at most N K of them -- are compacted into LDS,
+// where each is ranked by counting the larger ones.  Keys are unique, so the
+// ranks are distinct.
 template <int N>
 __device__ __forceinline__ void block_top_k(const uint64_t (&key)[N], int K, uint64_t *s_c,
                                             uint64_t *s_tmax, int *s_cnt, uint64_t *s_tau,
-                                            uint64_t *out) {
+                                            uint64_t *out, uint64_t floor_key = 0ull) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     uint64_t tmax = 0ull;
 #pragma unroll
@@ -95,7 +98,7 @@ __device__ __forceinline__ void block_top_k(const uint64_t (&key)[N], int K, uin
     }
     if (rank == K - 1 && tmax != 0ull) *s_tau = tmax;
     __syncthreads();
-    const uint64_t tau = *s_tau;
+    const uint64_t tau = max(*s_tau, floor_key);
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < N; j++) cnt += key[j] >= tau ? 1 : 0;
@@ -231,7 +234,36 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restri
             row_flag[m] = (any || !(l > -(double)kInf && l < (double)kInf)) ? (unsigned)TEV_FLAG_NONFINITE : 0u;
         }
     }
-    block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, &s_tau, top + m * (size_t)K);
+    // A floor for the row's K-th key: every slab list is sorted, best first,
+    // so the K-th largest of a pool of each list's first q keys (any K keys of
+    // the row) is at most the row's K-th key, and equals it when no list holds
+    // more than q of the row's K best.  Ranked by counting, as below.
+    __shared__ uint64_t s_floor;
+    const int q = min(K, (2 * K + ns - 1) / ns);
+    const int np = q * ns, np16 = (np + 15) & ~15;
+    uint64_t *s_pool = s_c;                           // free until the selection below
+    for (int e = tid; e < np16; e += TB_THREADS) {
+        const int l = e / q, p = e - l * q;
+        s_pool[e] = e < np ? cand[m * (size_t)nk + (size_t)l * K + p] : 0ull;
+    }
+    if (tid == 0) s_floor = 0ull;
+    __syncthreads();
+    for (int e = tid; e < np; e += TB_THREADS) {
+        const uint64_t x = s_pool[e];
+        if (x == 0ull) continue;
+        int r = 0;
+        for (int j = 0; j < np16; j += 16) {
+            uint64_t t[16];
+#pragma unroll
+            for (int u = 0; u < 16; u++) t[u] = s_pool[j + u];
+#pragma unroll
+            for (int u = 0; u < 16; u++) r += t[u] > x ? 1 : 0;
+        }
+        if (r == K - 1) s_floor = x;
+    }
+    __syncthreads();
+    const uint64_t floor_key = s_floor;
+    block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, &s_tau, top + m * (size_t)K, floor_key);
 }
 
 // The rank of depth d (1-based) packed big-endian: depths 1..8 in hi, 9..16 in lo.
@@ -676,7 +708,9 @@ hipError_t launch_typed(const void *z, const float *log_prior, double lp_default
     unsigned *row_flag = (unsigned *)(b + W.row_flag);
     k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(G * L)), TB_THREADS, ((size_t)TB_EPT * K + 16) * 8, st>>>(
         static_cast<const T *>(z), V, ns, K, flag, slab_m, slab_s, cand);
-    k_tb_rows<<<G * L, TB_THREADS, ((size_t)(8192 / TB_THREADS) * K + 16) * 8, st>>>(flag, slab_m, slab_s, cand, ns, K,
+    const int q_pool = std::min(K, (2 * K + ns - 1) / ns);           // the row merge's pool depth
+    const size_t rows_lds = std::max((size_t)(8192 / TB_THREADS) * K + 16, (size_t)((q_pool * ns + 15) & ~15)) * 8;
+    k_tb_rows<<<G * L, TB_THREADS, rows_lds, st>>>(flag, slab_m, slab_s, cand, ns, K,
                                                                                   top, lse, row_flag);
     unsigned *hstatus = M == 1 ? (unsigned *)(ws + MW.status) : (unsigned *)(b + W.status);
     StreamRec *strm = M == 1 ? nullptr : (StreamRec *)(ws + MW.stream);
