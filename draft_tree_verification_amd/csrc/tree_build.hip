@@ -24,13 +24,14 @@
 //   k_tb_rows   grid R*L, 256 threads: the union of the row's slab lists, 32
 //               keys per thread, through the same selection; writes the row's
 //               top K and its logsumexp (f64).
-//   k_tb_heap   grid R, one wave: the best-first search.  The frontier sits in
-//               registers, one slot per node holding that node's next child
-//               (ceil(B / 64) slots per lane); each pop is one DPP wave
-//               maximum over the keys in f32 with the exact order settled
-//               among the lanes that reach it, records a node, moves the
-//               winner's slot to the next sibling and opens the new node's
-//               slot with its rank-0 child.
+//   k_tb_heap   grid R, one wave: the best-first search.  The frontier has
+//               one slot per node holding that node's next child; a slot's
+//               key word sits in registers (ceil(B / 64) per lane) and the
+//               rest of it in an LDS record.  Each pop is one DPP wave
+//               maximum over the key words, exact stages among the slots
+//               that tie there, one read of the winner's record, and the
+//               winner's slot moved to the next sibling and the new node's
+//               slot opened with its rank-0 child.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -55,18 +56,10 @@ __device__ __forceinline__ float unord32(uint32_t o) {
 }
 __device__ __forceinline__ uint64_t ord64(double x) {
     const uint64_t u = (uint64_t)__double_as_longlong(x);
-    return (u >> 63) ? ~u : (u | (1ull << 63));
+    return u ^ ((uint64_t)((int64_t)u >> 63) | (1ull << 63));   // negative: all bits flipped; else the sign bit set
 }
 __device__ __forceinline__ uint64_t make_key(float x, int token) {
     return ((uint64_t)ord32(x) << 32) | (uint64_t)(~(uint32_t)token);
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t y = __shfl_xor(x, o);
-        x = y > x ? y : x;
-    }
-    return x;
 }
 
 // The K best of the keys the workgroup holds, N per thread (0 = no key),
@@ -266,10 +259,8 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restri
     block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, &s_tau, top + m * (size_t)K, floor_key);
 }
 
-// The rank of depth d (1-based) packed big-endian: depths 1..8 in hi, 9..16 in lo.
-__device__ __forceinline__ int rank_at(uint64_t hi, uint64_t lo, int d) {
-    return d <= 8 ? (int)((hi >> (8 * (8 - d))) & 255u) : (int)((lo >> (8 * (16 - d))) & 255u);
-}
+// Sets the rank of depth d (1-based) in a rank sequence packed big-endian:
+// depths 1..8 in hi, 9..16 in lo, one byte each.
 __device__ __forceinline__ void set_rank(uint64_t &hi, uint64_t &lo, int d, int r) {
     if (d <= 8) {
         const int sh = 8 * (8 - d);
@@ -287,26 +278,41 @@ struct StreamRec {
     int parent, token, depth, pad;
 };
 
-// Frontier slots.  Slot p (lane p mod 64, register p / 64) belongs to node
-// p and holds the next not yet emitted child of p: first its rank-0 child,
-// then, each time that child is popped, the next sibling.  So a pop changes
-// only the winner's own slot and the new node's slot, no slot is searched
-// for, and the parent of a slot's entry is the slot's node.
-struct Slot {
-    double s, sz, psz;      // key, logit sum of the path, logit sum of the parent's path
-    uint64_t hi, lo;        // rank sequence, depth d in byte d (big-endian, hi then lo)
-    float zn;               // logit of the next sibling's token (NaN: no next sibling)
-    int depth;              // 0: empty
-};
+// Frontier slots.  Slot p belongs to node p and holds the next not yet
+// emitted child of p: first its rank-0 child, then, each time that child is
+// popped, the next sibling.  So a pop changes only the winner's own slot and
+// the new node's slot, no slot is searched for, and the parent of a slot's
+// entry is the slot's node.
+//
+// Keys are compared as the order-preserving 64-bit image of the f64 key
+// (-0 folded into +0).  Only the high half sits in registers, one word per
+// slot (lane p mod 64, register p / 64; 0 = empty); the search takes its wave
+// maximum.  The rest of a slot is a record in LDS, read once per pop, so that
+// the pop's arithmetic starts from one LDS round trip: the logits of the
+// entry's token and of its next sibling's token, the entry's rank and depth,
+// the key's low half, the logit sum of the slot node's path, the depth
+// constants it needs (C_d, C_{d+1} and the rank-0 and rank-1 logits of depth
+// d + 1), and the slot node's rank sequence, parent and rank.  A key is
+// recomputed from the record with the arithmetic that made it, so it is the
+// same f64 value.
+//
+// Slots whose high halves tie are ordered exactly, by every tied lane at
+// once, in up to three wave maxima: the key's low half with the depth
+// (shorter first), then the rank sequence's depths 1..8, then its depths
+// 9..16 (smaller first, as big-endian bytes).
+__device__ __forceinline__ uint64_t heap_key(double s) { return ord64(s + 0.0); }
 
-// a before b in pop order: larger key, then shorter, then smaller rank sequence
-__device__ __forceinline__ bool before(const Slot &a, const Slot &b) {
-    if (a.depth == 0) return false;
-    if (b.depth == 0) return true;
-    if (a.s != b.s) return a.s > b.s;
-    if (a.depth != b.depth) return a.depth < b.depth;
-    if (a.hi != b.hi) return a.hi < b.hi;
-    return a.lo < b.lo;
+// Wave maximum: row maxima by in-row permutes, then row 0's into row 1 and
+// row 2's into row 3 (row_bcast:15), then row 1's into row 3 (row_bcast:31),
+// so lane 63 holds the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)wave::dpp_i<wave::kQuadXor1>((int)x));
+    x = max(x, (uint32_t)wave::dpp_i<wave::kQuadXor2>((int)x));
+    x = max(x, (uint32_t)wave::dpp_i<wave::kRowHalfMirror>((int)x));
+    x = max(x, (uint32_t)wave::dpp_i<wave::kRowMirror>((int)x));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xA, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
@@ -314,7 +320,37 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
 }
 
-// One wave per request; SLOTS = ceil(B / 64) slots per lane.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    return ((uint64_t)(uint32_t)wave::dpp_i<CTRL>((int)(uint32_t)(x >> 32)) << 32) |
+           (uint32_t)wave::dpp_i<CTRL>((int)(uint32_t)x);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = umax64(x, dpp_u64<wave::kQuadXor1>(x));
+    x = umax64(x, dpp_u64<wave::kQuadXor2>(x));
+    x = umax64(x, dpp_u64<wave::kRowHalfMirror>(x));
+    x = umax64(x, dpp_u64<wave::kRowMirror>(x));
+    return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+
+__device__ __forceinline__ double as_f64(int lo, int hi) {
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ int lo32(double x) { return (int)(uint32_t)__builtin_bit_cast(uint64_t, x); }
+__device__ __forceinline__ int hi32(double x) { return (int)(uint32_t)(__builtin_bit_cast(uint64_t, x) >> 32); }
+
+// A slot's record: {entry logit, next sibling's logit, rank | depth << 8, key
+// low half}, {logit sum of the slot node's path, C_d}, {C_{d+1}, rank-0 and
+// rank-1 logits of depth d + 1}, {the slot node's rank sequence: depths 1..8,
+// 9..16}, {the slot node's parent, its rank | depth << 8}.
+struct SlotRec {
+    int4 a, b, c, h;
+    int parent, rd, pad[2];
+};
+__device__ __forceinline__ uint64_t u64_of(int lo, int hi) { return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo; }
+
+// One wave per request; SLOTS = ceil(B / 64) key words per lane.
 template <int SLOTS>
 __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top, const double *__restrict__ lse,
                                                 const unsigned *__restrict__ row_flag,
@@ -326,9 +362,8 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
     constexpr int NLD = TB_MAX_L * TB_MAX_K / 64;     // top-K entries per lane
     __shared__ float s_tz[TB_MAX_L * TB_MAX_K];
     __shared__ int s_tt[TB_MAX_L * TB_MAX_K];
-    __shared__ int s_par[TEV_MAX_NODES], s_idx[TEV_MAX_NODES];
-    __shared__ double s_sc[TEV_MAX_NODES];
-    __shared__ uint64_t s_hi[TEV_MAX_NODES], s_lo[TEV_MAX_NODES];
+    __shared__ SlotRec s_rec[TEV_MAX_NODES + 1];     // + a scratch record for the first pop's deferred writes
+    __shared__ int4 s_dt[TB_MAX_L + 2];              // per depth e: C_e, rank-0 and rank-1 logits of depth e
     const int lane = threadIdx.x, r = blockIdx.x;
     const float qnan = __builtin_nanf("");
     // the mode's log prior: every key is (logit sum - logsumexp sum) + lp
@@ -352,16 +387,17 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
         }
     }
     const unsigned fl = __ballot(rf != 0u) != 0ull ? (unsigned)TEV_FLAG_NONFINITE : 0u;
-    // lane d holds C[d] = lse_0 + ... + lse_{d-1} (summed in order), and the
-    // rank-0 and rank-1 logits of depth d (position d)
+    // lane e holds C[e] = lse_0 + ... + lse_{e-1} (summed in order; 0 past L)
     double creg = 0.0, c = 0.0;
     for (int j = 0; j < L; j++) {
         c += wave::readlane_d(lse_l, j);
         if (lane == j + 1) creg = c;
     }
     __syncthreads();
+    // lane e: the rank-0 and rank-1 logits of depth e (NaN past L)
     const float zr0 = (lane >= 1 && lane <= L) ? s_tz[(lane - 1) * K] : qnan;
     const float zr1 = (lane >= 1 && lane <= L && K > 1) ? s_tz[(lane - 1) * K + 1] : qnan;
+    if (lane >= 1 && lane <= L + 1) s_dt[lane] = int4{lo32(creg), hi32(creg), __float_as_int(zr0), __float_as_int(zr1)};
     if (lane == 0) status[r] = fl;
     if (fl) {
         if (stream) {
@@ -375,135 +411,172 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
         }
         return;
     }
-    Slot f[SLOTS];
+    uint32_t fk[SLOTS];
 #pragma unroll
-    for (int q = 0; q < SLOTS; q++) f[q] = Slot{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
-    {   // the root's slot: its rank-0 child at position 1
-        const double sz = (double)wave::readlane_f(zr0, 1);
+    for (int q = 0; q < SLOTS; q++) fk[q] = 0u;
+    {   // the root's slot: its rank-0 child at position 1 (none under a NaN prior)
+        const float z0 = wave::readlane_f(zr0, 1), z1 = wave::readlane_f(zr1, 1);
+        const double c1 = wave::readlane_d(creg, 1), c2 = wave::readlane_d(creg, 2);
+        const float z02 = wave::readlane_f(zr0, 2), z12 = wave::readlane_f(zr1, 2);
+        const uint64_t k = heap_key(((0.0 + (double)z0) - c1) + lp);
         if (lane == 0) {
-            f[0].sz = sz;
-            f[0].s = (sz - wave::readlane_d(creg, 1)) + lp;
-            f[0].zn = wave::readlane_f(zr1, 1);
-            f[0].depth = 1;
+            fk[0] = lp == lp ? (uint32_t)(k >> 32) : 0u;
+            s_rec[0] = SlotRec{int4{__float_as_int(z0), __float_as_int(z1), 1 << 8, (int)(uint32_t)k},
+                               int4{lo32(0.0), hi32(0.0), lo32(c1), hi32(c1)},
+                               int4{lo32(c2), hi32(c2), __float_as_int(z02), __float_as_int(z12)},
+                               int4{0, 0, 0, 0}, -1, 0, {0, 0}};
         }
     }
+    // Two record parts wait one pop for their LDS loads: the winner's slot
+    // (its next sibling's next logit) and the new node's slot (the
+    // constants of depth d + 2).  Both are written after the next pop's wave
+    // maximum, before it reads any record.
+    int pend_p = TEV_MAX_NODES, pend_n = TEV_MAX_NODES, pend_rd = 0, pend_klo = 0;
+    bool pend_ok = false;
+    float pend_zc = 0.f, pend_zn2 = 0.f;
+    int4 pend_dt = int4{0, 0, 0, 0};
     int n = 1;
     for (; n < B; n++) {
-        int bq = 0;
-        Slot mine = f[0];
+        // maximum of the high halves over every slot, then the slots that reach it
+        uint32_t lm = fk[0];
 #pragma unroll
-        for (int q = 1; q < SLOTS; q++)
-            if (before(f[q], mine)) {
-                mine = f[q];
-                bq = q;
-            }
-        // coarse maximum in f32 (monotone rounding keeps the true maximum
-        // among the lanes that reach it), then the exact order among those
-        const float k32 = mine.depth ? (float)mine.s : -kInf;
-        const float m32 = wave::max_f32(k32);
-        uint64_t ball = __ballot(mine.depth != 0 && k32 == m32);
-        if (ball == 0ull) break;                         // the universe is exhausted
-        int wl = __ffsll((long long)ball) - 1;
-        ball &= ball - 1;
-        if (ball) {
-            Slot w;
-            w.s = wave::readlane_d(mine.s, wl);
-            w.hi = readlane_u64(mine.hi, wl);
-            w.lo = readlane_u64(mine.lo, wl);
-            w.depth = __builtin_amdgcn_readlane(mine.depth, wl);
-            while (ball) {
-                const int l = __ffsll((long long)ball) - 1;
-                ball &= ball - 1;
-                Slot e;
-                e.s = wave::readlane_d(mine.s, l);
-                e.hi = readlane_u64(mine.hi, l);
-                e.lo = readlane_u64(mine.lo, l);
-                e.depth = __builtin_amdgcn_readlane(mine.depth, l);
-                if (before(e, w)) {
-                    w = e;
-                    wl = l;
+        for (int q = 1; q < SLOTS; q++) lm = max(lm, fk[q]);
+        const uint32_t m = wave_max_u32(lm);
+        if (m == 0u) break;                              // the universe is exhausted
+        if (lane == 0) {
+            s_rec[pend_p].a = int4{__float_as_int(pend_zc), __float_as_int(pend_ok ? pend_zn2 : qnan), pend_rd, pend_klo};
+            s_rec[pend_n].c = pend_dt;
+        }
+        uint64_t hit[SLOTS];
+        int nhit = 0;
+#pragma unroll
+        for (int q = 0; q < SLOTS; q++) {
+            hit[q] = __ballot(fk[q] == m);
+            nhit += __popcll(hit[q]);
+        }
+        int wq = SLOTS - 1;
+        uint64_t wb = hit[SLOTS - 1];
+#pragma unroll
+        for (int q = SLOTS - 2; q >= 0; q--) {
+            wq = hit[q] ? q : wq;
+            wb = hit[q] ? hit[q] : wb;
+        }
+        int p = wq * 64 + __ffsll((long long)wb) - 1;
+        if (nhit > 1) {
+            // the exact order of the tied slots' entries, each lane taking
+            // the best of its own: (low half, shallower) larger, then rank
+            // sequence smaller
+            uint64_t b1 = 0ull, bhi = ~0ull, blo = ~0ull;
+            int bq = 0;
+            bool mine = false;
+#pragma unroll
+            for (int q = 0; q < SLOTS; q++) {
+                if ((hit[q] >> lane) & 1ull) {
+                    const SlotRec &R = s_rec[q * 64 + lane];
+                    const int4 ra = R.a, rh = R.h;
+                    const int ed = ra.z >> 8;
+                    uint64_t ehi = u64_of(rh.x, rh.y), elo = u64_of(rh.z, rh.w);
+                    set_rank(ehi, elo, ed, ra.z & 255);
+                    const uint64_t k1 = ((uint64_t)(uint32_t)ra.w << 32) | (uint32_t)(16 - ed);
+                    if (!mine || k1 > b1 || (k1 == b1 && (ehi < bhi || (ehi == bhi && elo < blo)))) {
+                        b1 = k1;
+                        bhi = ehi;
+                        blo = elo;
+                        bq = q;
+                        mine = true;
+                    }
                 }
             }
+            uint64_t cand = __ballot(mine);
+            const uint64_t m1 = wave_max_u64(mine ? b1 : 0ull);
+            cand &= __ballot(b1 == m1);
+            if (__popcll(cand) > 1) {
+                const bool in = (cand >> lane) & 1ull;
+                const uint64_t m2 = wave_max_u64(in ? ~bhi : 0ull);
+                cand &= __ballot(~bhi == m2);
+                if (__popcll(cand) > 1) {
+                    const bool in2 = (cand >> lane) & 1ull;
+                    const uint64_t m3 = wave_max_u64(in2 ? ~blo : 0ull);
+                    cand &= __ballot(~blo == m3);
+                }
+            }
+            const int l = __ffsll((long long)cand) - 1;      // distinct entries: one lane left
+            p = __builtin_amdgcn_readlane(bq, l) * 64 + l;
         }
-        const double ws = wave::readlane_d(mine.s, wl);
-        const double wsz = wave::readlane_d(mine.sz, wl);
-        const double wpsz = wave::readlane_d(mine.psz, wl);
-        const float wzn = wave::readlane_f(mine.zn, wl);
-        const uint64_t whi = readlane_u64(mine.hi, wl), wlo = readlane_u64(mine.lo, wl);
-        const int d = __builtin_amdgcn_readlane(mine.depth, wl);
-        const int wq = __builtin_amdgcn_readlane(bq, wl);
-        const int rk = rank_at(whi, wlo, d);
-        const int parent = wq * 64 + wl;                 // the slot's node
-        // Everything the two new slots need, as uniform values read at once:
-        // the constants of depths d and d + 1 (lanes 1..L; the child exists
-        // only for d < L) and the logit after the next sibling (LDS
-        // broadcast, clamped index).
-        const int d1 = min(d + 1, L);
-        const double cd = wave::readlane_d(creg, d), cd1 = wave::readlane_d(creg, d1);
-        const float z0 = wave::readlane_f(zr0, d1), z1 = wave::readlane_f(zr1, d1);
+        p = __builtin_amdgcn_readfirstlane(p);
+        // the winner's record: one LDS round trip (broadcast reads)
+        const SlotRec rec = s_rec[p];
+        __builtin_amdgcn_sched_barrier(0);               // all four parts in flight together
+        const int4 ra = rec.a, rb = rec.b, rc = rec.c;
+        const float zc = __int_as_float(ra.x), zn = __int_as_float(ra.y);
+        const int rd = ra.z, d = rd >> 8, rk = rd & 255;
+        const double psz = as_f64(rb.x, rb.y), cd = as_f64(rb.z, rb.w), cd1 = as_f64(rc.x, rc.y);
+        const float z0 = __int_as_float(rc.z), z1 = __int_as_float(rc.w);
+        // for the new node's slot: the constants of depth d + 2 (clamped);
+        // for the winner's slot: the logit after the next sibling (clamped)
+        const int4 dt2 = s_dt[min(d + 2, L + 1)];
         const float zn2 = s_tz[(d - 1) * K + min(rk + 2, K - 1)];
-        if (lane == 0) {
-            s_par[n] = parent;
-            s_idx[n] = (d - 1) * K + rk;
-            s_sc[n] = ws;
-            s_hi[n] = whi;
-            s_lo[n] = wlo;
-        }
+        const double wsz = psz + (double)zc;
         // the winner's slot moves on to the next sibling (or empties) ...
-        Slot sib{0.0, 0.0, 0.0, 0ull, 0ull, qnan, 0};
-        if (rk + 1 < K) {
-            sib.psz = wpsz;
-            sib.sz = wpsz + (double)wzn;
-            sib.s = (sib.sz - cd) + lp;
-            sib.hi = whi;
-            sib.lo = wlo;
-            set_rank(sib.hi, sib.lo, d, rk + 1);
-            sib.zn = rk + 2 < K ? zn2 : qnan;
-            sib.depth = d;
-        }
-        // ... and node n's slot starts with its rank-0 child (both computed
-        // by every lane, then moved into their owners' registers)
-        Slot ch;
-        ch.psz = wsz;
-        ch.sz = wsz + (double)z0;
-        ch.s = (ch.sz - cd1) + lp;
-        ch.hi = whi;                                      // rank 0 at depth d + 1: byte already 0
-        ch.lo = wlo;
-        ch.zn = z1;
-        ch.depth = d + 1;
-        if (lane == wl) {
+        const uint64_t sk = heap_key(((psz + (double)zn) - cd) + lp);
+        // ... and node n's slot starts with its rank-0 child (none at depth L)
+        const uint64_t ck = heap_key(((wsz + (double)z0) - cd1) + lp);
+        const uint32_t sk_hi = rk + 1 < K ? (uint32_t)(sk >> 32) : 0u;
+        const uint32_t ck_hi = d < L ? (uint32_t)(ck >> 32) : 0u;
+        const int wq2 = p >> 6, wl2 = p & 63, nq = n >> 6, nl = n & 63;
 #pragma unroll
-            for (int q = 0; q < SLOTS; q++)
-                if (q == wq) f[q] = sib;                 // wq is uniform: one branch taken
+        for (int q = 0; q < SLOTS; q++) {
+            if ((SLOTS == 1 || q == wq2) && lane == wl2) fk[q] = sk_hi;
+            if ((SLOTS == 1 || q == nq) && lane == nl) fk[q] = ck_hi;
         }
-        if (d < L && lane == (n & 63)) {
-#pragma unroll
-            for (int q = 0; q < SLOTS; q++)
-                if (q == (n >> 6)) f[q] = ch;
+        uint64_t nhi = u64_of(rec.h.x, rec.h.y), nlo = u64_of(rec.h.z, rec.h.w);   // node n's rank sequence
+        set_rank(nhi, nlo, d, rk);
+        if (lane == 0) {
+            s_rec[n].a = int4{__float_as_int(z0), __float_as_int(z1), (d + 1) << 8, (int)(uint32_t)ck};
+            s_rec[n].b = int4{lo32(wsz), hi32(wsz), rc.x, rc.y};
+            s_rec[n].h = int4{(int)(uint32_t)nhi, (int)(uint32_t)(nhi >> 32), (int)(uint32_t)nlo, (int)(uint32_t)(nlo >> 32)};
+            s_rec[n].parent = p;
+            s_rec[n].rd = rd;
         }
+        pend_p = p;
+        pend_n = n;
+        pend_zc = zn;
+        pend_zn2 = zn2;
+        pend_ok = rk + 2 < K;
+        pend_rd = rd + 1;
+        pend_klo = (int)(uint32_t)sk;
+        pend_dt = dt2;
     }
     __syncthreads();
+    // node i (1 <= i < n): parent and rank in its slot record; its key is
+    // (logit sum of its path - C_d) + lp, as it was made when it was an entry
     if (stream) {
         // the mode's pop order, for the merge across modes
         for (int i = 1 + lane; i < n; i += 64) {
-            StreamRec e;
-            e.key = s_sc[i];
-            e.hi = s_hi[i];
-            e.lo = s_lo[i];
-            e.parent = s_par[i];
-            e.token = s_tt[s_idx[i]];
-            e.depth = s_idx[i] / K + 1;
-            e.pad = 0;
-            stream[(size_t)r * B + i] = e;
+            const SlotRec e = s_rec[i];
+            const int d = e.rd >> 8;
+            StreamRec o;
+            o.key = (as_f64(e.b.x, e.b.y) - as_f64(s_dt[d].x, s_dt[d].y)) + lp;
+            o.hi = u64_of(e.h.x, e.h.y);
+            o.lo = u64_of(e.h.z, e.h.w);
+            o.parent = e.parent;
+            o.depth = d;
+            o.token = s_tt[(d - 1) * K + (e.rd & 255)];
+            o.pad = 0;
+            stream[(size_t)r * B + i] = o;
         }
         if (lane == 0) stream_n[r] = n;
         return;
     }
     for (int i = lane; i < B; i += 64) {
-        const bool ok = i == 0 || i < n;
-        parents[(size_t)r * B + i] = i == 0 ? -1 : (ok ? s_par[i] : -1);
-        tokens[(size_t)r * B + i] = i == 0 ? (root_tokens ? root_tokens[r] : 0) : (ok ? s_tt[s_idx[i]] : -1);
-        scores[(size_t)r * B + i] = i == 0 ? 0.0 : (ok ? s_sc[i] : (double)qnan);
+        const bool ok = i > 0 && i < n;
+        const SlotRec e = s_rec[ok ? i : 0];
+        const int d = max(e.rd >> 8, 1);
+        parents[(size_t)r * B + i] = ok ? e.parent : -1;
+        tokens[(size_t)r * B + i] = i == 0 ? (root_tokens ? root_tokens[r] : 0)
+                                           : (ok ? s_tt[(d - 1) * K + (e.rd & 255)] : -1);
+        scores[(size_t)r * B + i] = i == 0 ? 0.0
+                                           : (ok ? (as_f64(e.b.x, e.b.y) - as_f64(s_dt[d].x, s_dt[d].y)) + lp : (double)qnan);
     }
 }
 
