@@ -584,20 +584,29 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
 // The merged heap pops every mode's entries in that mode's own order, and all
 // entries together in one order: key, then depth, rank sequence, mode.  A
 // node is created at the first pop of each distinct prefix, in that order.
-// So the merge is a sort and a deduplication, done in parallel by one
-// workgroup per request:
-//   1. the entries' sort indices, bitonic-sorted in LDS by that order;
-//   2. canonical prefix ids, depth by depth: a prefix is (its parent's id,
-//      its token), inserted into an LDS hash table; a mode-local parent always
-//      has a smaller depth, so its id is known;
-//   3. the first sorted position of every prefix (LDS atomic minimum); the
-//      entries at their prefix's first position are the nodes, numbered by a
-//      block prefix sum in sorted order; the first B - 1 form the tree.
-constexpr int MG_THREADS = 1024;                     // one compare-exchange per thread and stage
-constexpr int MG_N = TB_MAX_MODES * TEV_MAX_NODES;   // entries, a power of two
+// So the merge is a merge of sorted lists and a deduplication, done in
+// parallel by one workgroup per request:
+//   1. each entry's place in the merged order: its place in its own mode's
+//      stream (already in that order) plus, for every other mode, the number
+//      of that stream's entries before it (a binary search; entries compare
+//      by the order-preserving bits of the key, and by depth, rank sequence
+//      and mode only when the keys are equal);
+//   2. canonical prefix ids, depth by depth over the entries bucketed by
+//      depth: a prefix is (its parent's id, its token), inserted into an LDS
+//      hash table; a mode-local parent always has a smaller depth, so its id
+//      is known;
+//   3. the first merged place of every prefix (LDS atomic minimum); the
+//      entries at their prefix's first place are the nodes, numbered by a
+//      block prefix sum in merged order; the first B - 1 form the tree.
+constexpr int MG_THREADS = 1024;
+constexpr int MG_N = TB_MAX_MODES * TEV_MAX_NODES;   // entries
 constexpr int MG_HASH = 2 * MG_N;                    // hash slots (load <= 1/2)
 constexpr int MG_ROOT = MG_HASH;                     // canonical id of the root prefix
-static_assert((MG_N & (MG_N - 1)) == 0, "bitonic sort over a power of two");
+constexpr int MG_EPT = MG_N / MG_THREADS;            // entries (and merged places) per thread
+
+__device__ __forceinline__ double unord64(uint64_t o) {
+    return __longlong_as_double((long long)(o ^ ((uint64_t)((int64_t)~o >> 63) | (1ull << 63))));
+}
 
 __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__restrict__ stream,
                                                          const int32_t *__restrict__ stream_n,
@@ -605,21 +614,25 @@ __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__rest
                                                          const int32_t *__restrict__ root_tokens, int M, int B,
                                                          unsigned *__restrict__ status, int32_t *__restrict__ parents,
                                                          int32_t *__restrict__ tokens, double *__restrict__ scores) {
-    constexpr int EPT = MG_N / MG_THREADS;            // sorted positions per thread
-    __shared__ double s_key[MG_N];
+    __shared__ uint64_t s_pk[MG_N];                   // order-preserving bits of the key
     __shared__ uint64_t s_rhi[MG_N], s_rlo[MG_N];
     __shared__ int s_tok[MG_N];
-    __shared__ int16_t s_par[MG_N], s_sidx[MG_N], s_cid[MG_N], s_pcid[MG_N], s_nid[MG_N];
+    __shared__ int16_t s_par[MG_N], s_sidx[MG_N], s_cid[MG_N], s_pcid[MG_N], s_nid[MG_N], s_dlist[MG_N];
     __shared__ uint8_t s_dep[MG_N];
     __shared__ uint64_t s_hkey[MG_HASH];
     __shared__ int s_first[MG_HASH];
     __shared__ int s_len[TB_MAX_MODES];
+    __shared__ int s_dcnt[TB_MAX_L + 1], s_doff[TB_MAX_L + 2], s_dfill[TB_MAX_L + 1];
     __shared__ int s_wsum[MG_THREADS / 64];
     __shared__ unsigned s_fl;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = blockIdx.x;
     const StreamRec *st = stream + (size_t)r * M * B;
     if (tid == 0) s_fl = 0u;
     if (tid < M) s_len[tid] = stream_n[(size_t)r * M + tid];
+    if (tid <= TB_MAX_L) {
+        s_dcnt[tid] = 0;
+        s_dfill[tid] = 0;
+    }
     __syncthreads();
     if (tid < M && mode_status[(size_t)r * M + tid] != 0u) atomicOr(&s_fl, (unsigned)TEV_FLAG_NONFINITE);
     // entry e = k B + i, i in [1, len_k): mode k's i-th pop
@@ -628,16 +641,16 @@ __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__rest
         const bool ok = e < M * B && i >= 1 && i < s_len[k];
         if (ok) {
             const StreamRec x = st[e];
-            s_key[e] = x.key;
+            s_pk[e] = ord64(x.key + 0.0);
             s_rhi[e] = x.hi;
             s_rlo[e] = x.lo;
             s_tok[e] = x.token;
             s_par[e] = (int16_t)x.parent;
             s_dep[e] = (uint8_t)x.depth;
+            atomicAdd(&s_dcnt[x.depth], 1);
         } else {
             s_dep[e] = 0;
         }
-        s_sidx[e] = (int16_t)(ok ? e : -1);
     }
     for (int h = tid; h < MG_HASH; h += MG_THREADS) {
         s_hkey[h] = 0ull;
@@ -654,37 +667,86 @@ __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__rest
         }
         return;
     }
-    // a before b in the merged heap's pop order; -1 (no entry) last
-    auto before_e = [&](int a, int b) __attribute__((always_inline)) {
-        if (a < 0) return false;
-        if (b < 0) return true;
-        const double ka = s_key[a], kb = s_key[b];
-        if (ka != kb) return ka > kb;
-        if (s_dep[a] != s_dep[b]) return s_dep[a] < s_dep[b];
-        if (s_rhi[a] != s_rhi[b]) return s_rhi[a] < s_rhi[b];
-        if (s_rlo[a] != s_rlo[b]) return s_rlo[a] < s_rlo[b];
-        return a / B < b / B;
-    };
-    // 1. bitonic sort of the entry indices, best first: pair p of a stage is
-    //    (i, i + j) with i = (p / j) 2j + p mod j
-    static_assert(MG_N == 2 * MG_THREADS, "one pair per thread");
-    for (int kk = 2; kk <= MG_N; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            const int i = 2 * tid - (tid & (j - 1));     // (tid / j) 2j + tid mod j, j a power of two
-            const int ij = i + j;
-            const int a = s_sidx[i], b = s_sidx[ij];
-            const bool up = (i & kk) == 0;
-            if (up ? before_e(b, a) : before_e(a, b)) {
-                s_sidx[i] = (int16_t)b;
-                s_sidx[ij] = (int16_t)a;
-            }
-            __syncthreads();
+    if (tid == 0) {
+        int o = 0;
+        for (int d = 0; d <= TB_MAX_L; d++) {
+            s_doff[d] = o;
+            o += s_dcnt[d];
         }
+        s_doff[TB_MAX_L + 1] = o;
     }
+    __syncthreads();
+    int nent = 0;                                     // entries over all modes
+#pragma unroll
+    for (int k = 0; k < TB_MAX_MODES; k++) nent += k < M ? max(s_len[k] - 1, 0) : 0;
+    // 1. merged places.  x before e: larger key, then shorter, then smaller
+    //    rank sequence, then smaller mode (x and e in different modes).
+    auto tie_before = [&](int x, int e) __attribute__((always_inline)) {
+        const int dx = s_dep[x], de = s_dep[e];
+        if (dx != de) return dx < de;
+        const uint64_t hx = s_rhi[x], he = s_rhi[e];
+        if (hx != he) return hx < he;
+        const uint64_t lx = s_rlo[x], le = s_rlo[e];
+        if (lx != le) return lx < le;
+        return x / B < e / B;
+    };
+    int len[TB_MAX_MODES];
+#pragma unroll
+    for (int k2 = 0; k2 < TB_MAX_MODES; k2++) len[k2] = k2 < M ? s_len[k2] : 0;
+    // c[t][k2]: entries 1..c of mode k2 come before the thread's t-th entry
+    // (stream order is the merged order within a mode, so the predicate
+    // holds on a prefix); every step loads all its probes before comparing
+    int ent[MG_EPT], ek[MG_EPT];
+    bool eok[MG_EPT];
+    uint64_t pe[MG_EPT];
+    int c[MG_EPT][TB_MAX_MODES];
+#pragma unroll
+    for (int t = 0; t < MG_EPT; t++) {
+        const int e = tid + t * MG_THREADS, k = e / B, i = e - k * B;
+        ent[t] = e;
+        ek[t] = k;
+        eok[t] = e < M * B && i >= 1 && i < len[min(k, TB_MAX_MODES - 1)];
+        pe[t] = s_pk[e];
+#pragma unroll
+        for (int k2 = 0; k2 < TB_MAX_MODES; k2++) c[t][k2] = 0;
+    }
+#pragma unroll
+    for (int step = TEV_MAX_NODES / 2; step >= 1; step >>= 1) {
+        uint64_t px[MG_EPT][TB_MAX_MODES];
+#pragma unroll
+        for (int t = 0; t < MG_EPT; t++)
+#pragma unroll
+            for (int k2 = 0; k2 < TB_MAX_MODES; k2++)
+                px[t][k2] = s_pk[k2 * B + min(c[t][k2] + step, max(len[k2] - 1, 0))];
+#pragma unroll
+        for (int t = 0; t < MG_EPT; t++)
+#pragma unroll
+            for (int k2 = 0; k2 < TB_MAX_MODES; k2++) {
+                const int j = c[t][k2] + step;
+                const bool probe = eok[t] && k2 != ek[t] && j < len[k2];
+                bool take = probe && px[t][k2] > pe[t];
+                if (probe && px[t][k2] == pe[t]) take = tie_before(k2 * B + j, ent[t]);
+                c[t][k2] = take ? j : c[t][k2];
+            }
+    }
+#pragma unroll
+    for (int t = 0; t < MG_EPT; t++) {
+        if (!eok[t]) continue;
+        const int e = ent[t];
+        int place = e - ek[t] * B - 1;
+#pragma unroll
+        for (int k2 = 0; k2 < TB_MAX_MODES; k2++) place += c[t][k2];
+        s_sidx[place] = (int16_t)e;
+        const int d = s_dep[e];
+        s_dlist[s_doff[d] + atomicAdd(&s_dfill[d], 1)] = (int16_t)e;
+    }
+    __syncthreads();
     // 2. canonical prefix ids, one depth at a time
     for (int d = 1; d <= TB_MAX_L; d++) {
-        for (int e = tid; e < M * B; e += MG_THREADS) {
-            if (s_dep[e] != d) continue;
+        const int n0 = s_doff[d], n1 = s_doff[d + 1];
+        if (n0 == n1) continue;                       // uniform: the same for every thread
+        for (int q = n0 + tid; q < n1; q += MG_THREADS) {
+            const int e = s_dlist[q];
             const int k = e / B;
             const int pl = s_par[e];
             const int pc = pl == 0 ? MG_ROOT : s_cid[k * B + pl];
@@ -700,19 +762,15 @@ __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__rest
         }
         __syncthreads();
     }
-    // 3. first sorted position of every prefix, then the nodes in sorted order
-    for (int pos = tid; pos < MG_N; pos += MG_THREADS) {
-        const int e = s_sidx[pos];
-        if (e >= 0) atomicMin(&s_first[s_cid[e]], pos);
-    }
+    // 3. first merged place of every prefix, then the nodes in merged order
+    for (int pos = tid; pos < nent; pos += MG_THREADS) atomicMin(&s_first[s_cid[s_sidx[pos]]], pos);
     __syncthreads();
     int cnt = 0;
-    bool first[EPT];
+    bool first[MG_EPT];
 #pragma unroll
-    for (int t = 0; t < EPT; t++) {
-        const int pos = tid * EPT + t;
-        const int e = s_sidx[pos];
-        first[t] = e >= 0 && s_first[s_cid[e]] == pos;
+    for (int t = 0; t < MG_EPT; t++) {
+        const int pos = tid * MG_EPT + t;
+        first[t] = pos < nent && s_first[s_cid[s_sidx[pos]]] == pos;
         cnt += first[t] ? 1 : 0;
     }
     int incl = cnt;
@@ -729,22 +787,22 @@ __global__ __launch_bounds__(MG_THREADS) void k_tb_merge(const StreamRec *__rest
 #pragma unroll
     for (int w = 0; w < MG_THREADS / 64; w++) total += s_wsum[w];
 #pragma unroll
-    for (int t = 0; t < EPT; t++) {
-        const int pos = tid * EPT + t;
+    for (int t = 0; t < MG_EPT; t++) {
+        const int pos = tid * MG_EPT + t;
         s_nid[pos] = (int16_t)(first[t] ? 1 + base : 0);
         base += first[t] ? 1 : 0;
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < EPT; t++) {
-        const int pos = tid * EPT + t;
+    for (int t = 0; t < MG_EPT; t++) {
+        const int pos = tid * MG_EPT + t;
         const int nid = s_nid[pos];
         if (nid >= 1 && nid < B) {
             const int e = s_sidx[pos];
             const int pc = s_pcid[e];
             parents[(size_t)r * B + nid] = pc == MG_ROOT ? 0 : s_nid[s_first[pc]];
             tokens[(size_t)r * B + nid] = s_tok[e];
-            scores[(size_t)r * B + nid] = s_key[e];
+            scores[(size_t)r * B + nid] = unord64(s_pk[e]);
         }
     }
     for (int i = tid; i < B; i += MG_THREADS) {
