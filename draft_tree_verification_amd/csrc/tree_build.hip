@@ -62,69 +62,169 @@ __device__ __forceinline__ uint64_t make_key(float x, int token) {
     return ((uint64_t)ord32(x) << 32) | (uint64_t)(~(uint32_t)token);
 }
 
+// Wave-wide bitwise AND and OR, and an inclusive prefix sum over the lanes
+// (in-row steps by DPP, then the totals of the rows before).
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t x) {
+    x &= (uint32_t)wave::dpp_i<wave::kQuadXor1>((int)x);
+    x &= (uint32_t)wave::dpp_i<wave::kQuadXor2>((int)x);
+    x &= (uint32_t)wave::dpp_i<wave::kRowHalfMirror>((int)x);
+    x &= (uint32_t)wave::dpp_i<wave::kRowMirror>((int)x);
+    return ((uint32_t)__builtin_amdgcn_readlane((int)x, 0) & (uint32_t)__builtin_amdgcn_readlane((int)x, 16)) &
+           ((uint32_t)__builtin_amdgcn_readlane((int)x, 32) & (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t x) {
+    x |= (uint32_t)wave::dpp_i<wave::kQuadXor1>((int)x);
+    x |= (uint32_t)wave::dpp_i<wave::kQuadXor2>((int)x);
+    x |= (uint32_t)wave::dpp_i<wave::kRowHalfMirror>((int)x);
+    x |= (uint32_t)wave::dpp_i<wave::kRowMirror>((int)x);
+    return ((uint32_t)__builtin_amdgcn_readlane((int)x, 0) | (uint32_t)__builtin_amdgcn_readlane((int)x, 16)) |
+           ((uint32_t)__builtin_amdgcn_readlane((int)x, 32) | (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+}
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+    x += __builtin_amdgcn_mov_dpp(x, wave::kRowShr + 1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, wave::kRowShr + 2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, wave::kRowShr + 4, 0xF, 0xF, true);
+    x += __builtin_amdgcn_mov_dpp(x, wave::kRowShr + 8, 0xF, 0xF, true);
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = lane >> 4;
+    return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2);
+}
+
+// Radix select of the K-th largest of the 32-bit values v[i] that are in the
+// set (in[i]), by the whole wave, most significant bit first, over the bits on
+// which those values differ (bits they all share are the answer's).  rem: K
+// on entry, the rank of the answer among the set's values equal to it on
+// return (1 = the first of them).
+template <int VPL>
+__device__ __forceinline__ uint32_t wave_radix_select(const uint32_t (&v)[VPL], const bool (&in)[VPL], int &rem) {
+    uint32_t a = ~0u, o = 0u;
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        a &= in[i] ? v[i] : ~0u;
+        o |= in[i] ? v[i] : 0u;
+    }
+    const uint32_t all1 = wave_and_u32(a), any1 = wave_or_u32(o);
+    uint32_t vary = all1 ^ any1, prefix = all1, mask = ~vary;
+    while (vary) {
+        const uint32_t bit = 1u << (31 - __clz((int)vary));
+        vary &= ~bit;
+        const uint32_t m = mask | bit, cand = prefix | bit;
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; i++) cnt += __popcll(__ballot(in[i] && (v[i] & m) == cand));
+        if (cnt >= rem)
+            prefix = cand;
+        else
+            rem -= cnt;
+        mask = m;
+    }
+    return prefix;
+}
+
+// The K-th largest high half th of the 64 VPL values v (with multiplicity;
+// K <= 64 VPL), by the whole wave; rem returns the answer's rank among the
+// values whose high half is th.
+template <int VPL>
+__device__ __forceinline__ uint32_t wave_kth_high(const uint64_t (&v)[VPL], int K, int &rem) {
+    uint32_t h[VPL];
+    bool in[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        h[i] = (uint32_t)(v[i] >> 32);
+        in[i] = true;
+    }
+    rem = K;
+    return wave_radix_select<VPL>(h, in, rem);
+}
+// The K-th largest of the values v, given th and rem from wave_kth_high: the
+// low halves of the values whose high half is th.
+template <int VPL>
+__device__ __forceinline__ uint64_t wave_kth_exact(const uint64_t (&v)[VPL], uint32_t th, int rem) {
+    uint32_t l[VPL];
+    bool in[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; i++) {
+        l[i] = (uint32_t)v[i];
+        in[i] = (uint32_t)(v[i] >> 32) == th;
+    }
+    return ((uint64_t)th << 32) | wave_radix_select<VPL>(l, in, rem);
+}
+
 // The K best of the keys the workgroup holds, N per thread (0 = no key),
-// written best first to out[0..K) (0 past the last key).  The K-th largest
-// per-thread maximum bounds the K-th key from below (K threads hold a key at
-// least that large), and so does the caller's floor (0: none); only keys at or
-// above the larger bound -- at most N K of them -- are compacted into LDS,
-// where each is ranked by counting the larger ones.  Keys are unique, so the
-// ranks are distinct.
+// written best first to out[0..K) (0 past the last key).  K threads hold a key
+// whose high half is at least th, the K-th largest high half of the
+// per-thread maxima, so the K-th key is at least th << 32; the caller's floor
+// (0: none) bounds it from below too.  The keys at or above the larger bound
+// are compacted into LDS, where each is ranked by counting the larger ones;
+// should they be more than N K (maxima tied on their high halves), the bound
+// becomes the K-th largest maximum itself, which at most K threads reach.
+// Keys are unique, so the ranks are distinct.
 template <int N>
-__device__ __forceinline__ void block_top_k(const uint64_t (&key)[N], int K, uint64_t *s_c,
-                                            uint64_t *s_tmax, int *s_cnt, uint64_t *s_tau,
-                                            uint64_t *out, uint64_t floor_key = 0ull) {
+__device__ __forceinline__ void block_top_k(const uint64_t (&key)[N], int K, uint64_t *s_c, uint64_t *s_tmax,
+                                            int *s_cnt, uint64_t *out, uint64_t floor_key = 0ull) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    static_assert(TB_THREADS == 256, "four maxima per lane of one wave");
     uint64_t tmax = 0ull;
 #pragma unroll
     for (int j = 0; j < N; j++) tmax = key[j] > tmax ? key[j] : tmax;
     s_tmax[tid] = tmax;
-    if (tid == 0) *s_tau = 1ull;
     __syncthreads();
-    // in batches of 16 broadcast reads, all issued before the first compare
-    int rank = 0;
-    for (int j = 0; j < TB_THREADS; j += 16) {
-        uint64_t t[16];
+    // every wave selects the same bound from the 256 maxima
+    uint64_t tv[4];
 #pragma unroll
-        for (int u = 0; u < 16; u++) t[u] = s_tmax[j + u];
+    for (int i = 0; i < 4; i++) tv[i] = s_tmax[4 * lane + i];
+    int rem;
+    const uint32_t th = wave_kth_high<4>(tv, K, rem);
+    uint64_t tau = (uint64_t)th << 32;
+    int cnt, incl, n, pass = 0;
+    for (;; pass++) {
+        tau = tau > floor_key ? tau : floor_key;
+        tau = tau > 1ull ? tau : 1ull;                // 0 is no key
+        cnt = 0;
 #pragma unroll
-        for (int u = 0; u < 16; u++) rank += t[u] > tmax ? 1 : 0;
+        for (int j = 0; j < N; j++) cnt += key[j] >= tau ? 1 : 0;
+        incl = wave_incl_scan_i32(cnt, lane);
+        if (lane == 63) s_cnt[wv + 4 * pass] = incl;
+        __syncthreads();
+        n = 0;
+#pragma unroll
+        for (int w = 0; w < TB_THREADS / 64; w++) n += s_cnt[w + 4 * pass];
+        if (pass == 1 || n <= N * K) break;           // uniform
+        tau = wave_kth_exact<4>(tv, th, rem);
     }
-    if (rank == K - 1 && tmax != 0ull) *s_tau = tmax;
-    __syncthreads();
-    const uint64_t tau = max(*s_tau, floor_key);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < N; j++) cnt += key[j] >= tau ? 1 : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_cnt[wv] = incl;
-    __syncthreads();
     int pos = incl - cnt;
-    for (int w = 0; w < wv; w++) pos += s_cnt[w];
-    int n = 0;
+    for (int w = 0; w < wv; w++) pos += s_cnt[w + 4 * pass];
+    // every key is stored, the others to the wave's lane slot past the
+    // N K + 16 compacted ones, so no store waits on a branch
+    const int spare = N * K + 16 + tid;
 #pragma unroll
-    for (int w = 0; w < TB_THREADS / 64; w++) n += s_cnt[w];
-#pragma unroll
-    for (int j = 0; j < N; j++)
-        if (key[j] >= tau) s_c[pos++] = key[j];
+    for (int j = 0; j < N; j++) {
+        const bool c = key[j] >= tau;
+        s_c[c ? pos : spare] = key[j];
+        pos += c ? 1 : 0;
+    }
     const int n16 = (n + 15) & ~15;                   // zero padding: never above a key
     for (int i = n + tid; i < n16; i += TB_THREADS) s_c[i] = 0ull;
     __syncthreads();
-    for (int i = tid; i < n; i += TB_THREADS) {
-        const uint64_t c = s_c[i];
+    // rank by counting; with few keys, G adjacent lanes share a key's count
+    const int G = n <= TB_THREADS / 4 ? 4 : n <= TB_THREADS / 2 ? 2 : 1;   // uniform
+    const int seg = ((n16 / G) + 15) & ~15;
+    for (int i0 = 0; i0 < n; i0 += TB_THREADS / G) {
+        const int i = i0 + tid / G, g = tid % G;
+        const uint64_t c = i < n ? s_c[i] : 0ull;
         int r = 0;
-        for (int j = 0; j < n16; j += 16) {
-            uint64_t t[16];
+        const int j1 = min(n16, (g + 1) * seg);
+        for (int j = g * seg; j < j1; j += 16) {
+            ulonglong2 t[8];
 #pragma unroll
-            for (int u = 0; u < 16; u++) t[u] = s_c[j + u];
+            for (int u = 0; u < 8; u++) t[u] = *reinterpret_cast<const ulonglong2 *>(s_c + j + 2 * u);
 #pragma unroll
-            for (int u = 0; u < 16; u++) r += t[u] > c ? 1 : 0;
+            for (int u = 0; u < 8; u++) r += (t[u].x > c ? 1 : 0) + (t[u].y > c ? 1 : 0);
         }
-        if (r < K) out[r] = c;
+        if (G >= 2) r += wave::dpp_i<wave::kQuadXor1>(r);
+        if (G == 4) r += wave::dpp_i<wave::kQuadXor2>(r);
+        if (i < n && g == 0 && r < K) out[r] = c;
     }
     for (int i = n + tid; i < K; i += TB_THREADS) out[i] = 0ull;
 }
@@ -138,12 +238,11 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
     constexpr int VW = 16 / (int)sizeof(T);
     constexpr int SPAN = TB_THREADS * VW;
     constexpr int NWV = TB_THREADS / 64;
-    extern __shared__ uint64_t s_c[];                 // TB_EPT * K keys + 16 of padding
+    extern __shared__ __align__(16) uint64_t s_c[];   // TB_EPT * K keys, 16 of padding, a spare slot per thread
     __shared__ uint64_t s_tmax[TB_THREADS];
     __shared__ float s_max[NWV];
     __shared__ double s_sum[NWV];
-    __shared__ int s_cnt[NWV];
-    __shared__ uint64_t s_tau;
+    __shared__ int s_cnt[2 * NWV];                   // per wave, two passes
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, s = blockIdx.x;
     const size_t m = blockIdx.y;
     const int start = s * TB_SLAB, len = min(TB_SLAB, V - start);
@@ -175,13 +274,18 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_slabs(const T *__restrict__ z
             const int idx = k * SPAN + tid * VW + j;
             key[k * VW + j] = idx < len ? make_key(x[k * VW + j], start + idx) : 0ull;
         }
-    block_top_k<TB_EPT>(key, K, s_c, s_tmax, s_cnt, &s_tau, cand + (m * ns + s) * (size_t)K);
+    block_top_k<TB_EPT>(key, K, s_c, s_tmax, s_cnt, cand + (m * ns + s) * (size_t)K);
     if (tid == 0) {
         slab_m[m * ns + s] = mx;
         slab_s[m * ns + s] = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
         flag[m * ns + s] = any_bad ? (unsigned)TEV_FLAG_NONFINITE : 0u;
     }
 }
+
+// The row merge's floor pool: q = min(K, ceil(2 K / ns)) keys of each of the
+// ns slab lists, q ns <= 2 K + ns keys.
+constexpr int TB_POOL = 384;
+static_assert(2 * TB_MAX_K + TB_MAX_SLABS <= TB_POOL && TB_POOL % 64 == 0, "the floor pool fits the wave");
 
 // One row: the union of its slab lists (ns K <= 8192 keys, 32 per thread) and
 // the row's logsumexp from the slab partials.
@@ -193,10 +297,9 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restri
                                                         unsigned *__restrict__ row_flag) {
     constexpr int NWV = TB_THREADS / 64;
     constexpr int NK = 8192 / TB_THREADS;
-    extern __shared__ uint64_t s_c[];                 // NK * K keys + 16 of padding
+    extern __shared__ __align__(16) uint64_t s_c[];   // NK * K keys, 16 of padding, a spare slot per thread
     __shared__ uint64_t s_tmax[TB_THREADS];
-    __shared__ int s_cnt[NWV];
-    __shared__ uint64_t s_tau;
+    __shared__ int s_cnt[2 * NWV];                   // per wave, two passes
     const int tid = threadIdx.x, lane = tid & 63;
     const size_t m = blockIdx.x;
     const int nk = ns * K;
@@ -230,33 +333,19 @@ __global__ __launch_bounds__(TB_THREADS) void k_tb_rows(const unsigned *__restri
     // A floor for the row's K-th key: every slab list is sorted, best first,
     // so the K-th largest of a pool of each list's first q keys (any K keys of
     // the row) is at most the row's K-th key, and equals it when no list holds
-    // more than q of the row's K best.  Ranked by counting, as below.
-    __shared__ uint64_t s_floor;
+    // more than q of the row's K best.  Every wave selects it from the pool's
+    // keys (0 past the pool: never above a key).
     const int q = min(K, (2 * K + ns - 1) / ns);
-    const int np = q * ns, np16 = (np + 15) & ~15;
-    uint64_t *s_pool = s_c;                           // free until the selection below
-    for (int e = tid; e < np16; e += TB_THREADS) {
-        const int l = e / q, p = e - l * q;
-        s_pool[e] = e < np ? cand[m * (size_t)nk + (size_t)l * K + p] : 0ull;
-    }
-    if (tid == 0) s_floor = 0ull;
-    __syncthreads();
-    for (int e = tid; e < np; e += TB_THREADS) {
-        const uint64_t x = s_pool[e];
-        if (x == 0ull) continue;
-        int r = 0;
-        for (int j = 0; j < np16; j += 16) {
-            uint64_t t[16];
+    const int np = q * ns;                            // <= 2 K + ns <= TB_POOL
+    uint64_t pv[TB_POOL / 64];
 #pragma unroll
-            for (int u = 0; u < 16; u++) t[u] = s_pool[j + u];
-#pragma unroll
-            for (int u = 0; u < 16; u++) r += t[u] > x ? 1 : 0;
-        }
-        if (r == K - 1) s_floor = x;
+    for (int i = 0; i < TB_POOL / 64; i++) {
+        const int e = i * 64 + lane, l = e / q, p = e - l * q;
+        pv[i] = e < np ? cand[m * (size_t)nk + (size_t)l * K + p] : 0ull;
     }
-    __syncthreads();
-    const uint64_t floor_key = s_floor;
-    block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, &s_tau, top + m * (size_t)K, floor_key);
+    int frem;
+    const uint64_t floor_key = (uint64_t)wave_kth_high<TB_POOL / 64>(pv, K, frem) << 32;
+    block_top_k<NK>(key, K, s_c, s_tmax, s_cnt, top + m * (size_t)K, floor_key);
 }
 
 // Sets the rank of depth d (1-based) in a rank sequence packed big-endian:
@@ -837,11 +926,9 @@ hipError_t launch_typed(const void *z, const float *log_prior, double lp_default
     uint64_t *top = (uint64_t *)(b + W.top);
     double *lse = (double *)(b + W.lse);
     unsigned *row_flag = (unsigned *)(b + W.row_flag);
-    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(G * L)), TB_THREADS, ((size_t)TB_EPT * K + 16) * 8, st>>>(
+    k_tb_slabs<T, VEC><<<dim3((unsigned)ns, (unsigned)(G * L)), TB_THREADS, ((size_t)TB_EPT * K + 16 + TB_THREADS) * 8, st>>>(
         static_cast<const T *>(z), V, ns, K, flag, slab_m, slab_s, cand);
-    const int q_pool = std::min(K, (2 * K + ns - 1) / ns);           // the row merge's pool depth
-    const size_t rows_lds = std::max((size_t)(8192 / TB_THREADS) * K + 16, (size_t)((q_pool * ns + 15) & ~15)) * 8;
-    k_tb_rows<<<G * L, TB_THREADS, rows_lds, st>>>(flag, slab_m, slab_s, cand, ns, K,
+    k_tb_rows<<<G * L, TB_THREADS, ((size_t)(8192 / TB_THREADS) * K + 16 + TB_THREADS) * 8, st>>>(flag, slab_m, slab_s, cand, ns, K,
                                                                                   top, lse, row_flag);
     unsigned *hstatus = M == 1 ? (unsigned *)(ws + MW.status) : (unsigned *)(b + W.status);
     StreamRec *strm = M == 1 ? nullptr : (StreamRec *)(ws + MW.stream);
