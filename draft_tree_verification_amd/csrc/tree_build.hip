@@ -387,8 +387,9 @@ struct StreamRec {
 //
 // Slots whose high halves tie are ordered exactly, by every tied lane at
 // once, in up to three wave maxima: the key's low half with the depth
-// (shorter first), then the rank sequence's depths 1..8, then its depths
-// 9..16 (smaller first, as big-endian bytes).
+// (shorter first) and the ranks of depths 1..4 (smaller first), then the rank
+// sequence's depths 1..8, then its depths 9..16 (smaller first, as big-endian
+// bytes).
 __device__ __forceinline__ uint64_t heap_key(double s) { return ord64(s + 0.0); }
 
 // Wave maximum: row maxima by in-row permutes, then row 0's into row 1 and
@@ -566,7 +567,13 @@ __global__ __launch_bounds__(64) void k_tb_heap(const uint64_t *__restrict__ top
                     const int ed = ra.z >> 8;
                     uint64_t ehi = u64_of(rh.x, rh.y), elo = u64_of(rh.z, rh.w);
                     set_rank(ehi, elo, ed, ra.z & 255);
-                    const uint64_t k1 = ((uint64_t)(uint32_t)ra.w << 32) | (uint32_t)(16 - ed);
+                    // key low half, then depth and the ranks of depths 1..4 as
+                    // 7-bit digits (ranks < 128), both inverted: smaller first
+                    const uint32_t t4 = (uint32_t)(ehi >> 32);
+                    const uint32_t dig = ((t4 >> 24) << 21) | (((t4 >> 16) & 255u) << 14) |
+                                         (((t4 >> 8) & 255u) << 7) | (t4 & 255u);
+                    const uint64_t k1 = ((uint64_t)(uint32_t)ra.w << 32) |
+                                        ((uint32_t)(16 - ed) << 28) | (~dig & 0x0FFFFFFFu);
                     if (!mine || k1 > b1 || (k1 == b1 && (ehi < bhi || (ehi == bhi && elo < blo)))) {
                         b1 = k1;
                         bhi = ehi;
