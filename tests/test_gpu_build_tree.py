@@ -111,6 +111,18 @@ def test_equal_logits_tie_order():
     np.testing.assert_array_equal(tok[0], [0, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1, 2, 0, 1])
 
 
+def test_equal_logits_over_many_slabs():
+    """Every logit equal over V = 300000 (37 slabs): the per-thread maxima of a
+    slab, and the slab lists of a row, all tie on their logit, so more keys
+    than the selection's buffer holds reach the bound taken from the logits
+    alone; the bound then becomes the exact K-th largest maximum.  The K
+    kept tokens of each position are the K smallest ids."""
+    z = np.full((2, 3, 300000), 0.5, np.float32)
+    z[1, 1, :] = -2.0
+    _compare(z, "f32", 4, 21)
+    _compare(W.f32_to_bf16_bits(z), "bf16", 4, 21)
+
+
 def test_heavy_bf16_ties():
     """bf16 logits on a coarse grid: many tokens share a logit, so ranks are
     decided by token id and many prefixes tie exactly."""
