@@ -86,6 +86,43 @@ def test_round_small(case):
     GP.log(f"[round] {name} ok, attention row error {err:.3e}")
 
 
+def _sweep_cases(n=48, seed=2026):
+    """Seeded random shapes across the launch plans: requests, tree size and
+    kind, vocabulary (odd sizes included), GQA ratio, head_dim, prefix length
+    around the 64-key stages and split boundaries (P = 0 included); sized so
+    that the oracle's attention stays within a few GFLOP per case."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        R = int(rng.integers(1, 13))
+        B = int(rng.choice([1, 2, 3, 17, 40, 64, 65, 127, 128, 200, 256]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        D = int(rng.choice([64, 128]))
+        P = int(rng.choice([0, 1, 31, 63, 64, 65, 255, 513, 1500, 2048, 4097]))
+        V = int(rng.integers(2000, 30001))
+        tree = str(rng.choice(["random", "chain", "star", "best_first"] if B >= 3 else ["random"]))
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        if R * B > 1200 or G * Hkv > 32 or R * B * G * Hkv * (P + B) * D > 1e9:
+            continue
+        cases.append(dict(name=f"sweep{len(cases)}", R=R, B=B, V=V, Hq=G * Hkv, Hkv=Hkv, D=D, P=P,
+                          tree=tree, dtype=dtype, seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c["name"] for c in SWEEP])
+def test_round_sweep(case):
+    c = dict(case)
+    name = c.pop("name")
+    GP.log(f"[round] {name} {c}")
+    wl = W.make_custom(name, n_uniform=512, **c)
+    err = _check_round(wl)
+    GP.log(f"[round] {name} ok, attention row error {err:.3e}")
+
+
 NAMED = ["tiny", "qwen3_4b", "qwen3_8b_wide", "mixture", "batched"]
 
 
