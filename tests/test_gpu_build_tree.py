@@ -256,3 +256,59 @@ def test_mixture_workload_modes():
     z = W.draft_rows_modes("mixture")
     GP.log(f"[build_tree_modes] mixture M={z.shape[1]} L={z.shape[2]} V={z.shape[3]} K=128 B=256")
     assert _compare_modes(z, "bf16", 128, 256) >= 1
+
+
+# ----------------------------------------------------------------------------
+# Seeded random shapes for both builders: rows, positions, vocabulary (odd
+# sizes, one-logit last slabs), retained tokens K, nodes B, logit spread
+# (peaked to flat) and dtype; the modes share a random part of their logits.
+def _universe(K, L):
+    return sum(K ** d for d in range(1, L + 1))
+
+
+def _sweep_builder_cases(n, modes, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        R = int(rng.integers(1, 6))
+        L = int(rng.integers(1, 17))
+        V = int(rng.choice([int(rng.integers(200, 5000)), int(rng.integers(5000, 40000)), 8193, 16385]))
+        K = int(rng.choice([1, 2, 3, 7, 8, 16, 31, 64, 100, 128]))
+        B = int(rng.choice([2, 3, 17, 63, 64, 65, 100, 128, 200, 256]))
+        M = int(rng.integers(1, 9)) if modes else 1
+        if K > V or M * _universe(K, L) < B - 1 or R * M * L * V > 4_000_000:
+            continue
+        cases.append(dict(R=R, M=M, L=L, V=V, K=K, B=B, sigma=float(rng.choice([0.5, 1.0, 3.0, 6.0])),
+                          dtype="bf16" if rng.random() < 0.5 else "f32", seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+SWEEP_ONE = _sweep_builder_cases(24, False, 7001)
+SWEEP_MODES = _sweep_builder_cases(16, True, 7002)
+
+
+def _sweep_logits(c, shape):
+    rng = np.random.default_rng(c["seed"])
+    z = (rng.standard_normal(shape) * c["sigma"]).astype(np.float32)
+    return z if c["dtype"] == "f32" else W.f32_to_bf16_bits(z)
+
+
+@pytest.mark.parametrize("case", SWEEP_ONE, ids=[f"sweep{i}" for i in range(len(SWEEP_ONE))])
+def test_build_tree_sweep(case):
+    GP.log(f"[build_tree] {case}")
+    z = _sweep_logits(case, (case["R"], case["L"], case["V"]))
+    _compare(z, case["dtype"], case["K"], case["B"], seed=case["seed"])
+
+
+@pytest.mark.parametrize("case", SWEEP_MODES, ids=[f"sweep{i}" for i in range(len(SWEEP_MODES))])
+def test_merged_heap_sweep(case):
+    GP.log(f"[build_tree_modes] {case}")
+    R, M = case["R"], case["M"]
+    z = _sweep_logits(case, (R, M, case["L"], case["V"]))
+    if M > 1:
+        # modes agree on part of the vocabulary, so prefixes recur across modes
+        rng = np.random.default_rng(case["seed"] + 1)
+        share = rng.uniform(size=z[:, 1:].shape) < 0.5
+        z[:, 1:] = np.where(share, z[:, :1], z[:, 1:])
+    lp = np.log(np.random.default_rng(case["seed"] + 2).dirichlet(np.ones(M), size=R)).astype(np.float32)
+    _compare_modes(z, case["dtype"], case["K"], case["B"], lp if case["seed"] % 2 else None, seed=case["seed"])
