@@ -97,3 +97,38 @@ def test_value_ranges(case):
     wl.v = W.f32_to_bf16_bits(v.astype(np.float32))
     err = GP.check_attn(wl)
     GP.log(f"[attn] {case} ok max row error {err:.3e}")
+
+
+def _sweep_cases(n=32, seed=3101):
+    """Seeded random shapes: requests, tree size and kind, GQA ratio, head_dim,
+    prefix length around the 64-key stages and the split plan's boundaries
+    (P = 0 and several thousand keys included), a fifth in f32."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        R = int(rng.integers(1, 17))
+        B = int(rng.choice([1, 2, 5, 16, 33, 64, 65, 100, 128, 129, 200, 256]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        P = int(rng.choice([0, 1, 2, 33, 64, 127, 128, 129, 288, 1000, 2047, 4097, 6000]))
+        tree = str(rng.choice(["random", "chain", "star", "best_first"] if B >= 3 else ["random"]))
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        if G * Hkv > 64 or R * B * G * Hkv * (P + B) * D > 1.5e9:
+            continue
+        cases.append(dict(name=f"sweep{len(cases)}", R=R, B=B, Hq=G * Hkv, Hkv=Hkv, D=D, P=P,
+                          tree=tree, dtype=dtype, seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c["name"] for c in SWEEP])
+def test_sweep(case):
+    c = dict(case)
+    name = c.pop("name")
+    GP.log(f"[attn] {name} {c}")
+    wl = W.make_custom(name, V=300, n_uniform=1, **c)
+    err = GP.check_attn(wl)
+    GP.log(f"[attn] {name} ok max row error {err:.3e}")

@@ -64,3 +64,33 @@ def test_commit_rejects_invalid_exit_node():
     assert np.all(nl == -1)
     np.testing.assert_array_equal(kg, kk)
     np.testing.assert_array_equal(vg, vv)
+
+
+def _sweep_cases(n=16, seed=3103):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        c = dict(dtype="f32" if rng.random() < 0.4 else "bf16", R=int(rng.integers(1, 7)),
+                 B=int(rng.choice([1, 2, 17, 64, 65, 130, 256])), L=int(rng.integers(1, 5)),
+                 Hkv=int(rng.choice([1, 2, 4, 8])), D=int(rng.choice([64, 128])),
+                 P=int(rng.choice([0, 1, 63, 64, 500, 2049])), tree=str(rng.choice(["random", "chain"])))
+        if c["L"] * c["R"] * c["Hkv"] * (c["P"] + c["B"]) * c["D"] > 6_000_000:
+            continue
+        c["seed"] = int(rng.integers(1, 1 << 30))
+        cases.append(c)
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"sweep{i}" for i in range(len(SWEEP))])
+def test_commit_sweep(case):
+    GP.log(f"[commit] {case}")
+    deepest = lambda par, rng: int(np.argmax(W.depths_of(par)))
+    for fn in (deepest, lambda par, rng: int(rng.integers(0, len(par)))):
+        kk, vv, par, en, kg, vg, nl = _run(exit_fn=fn, **case)
+        k2, v2, nl2 = oracle.commit_kv(kk, vv, par, en, case["P"])
+        np.testing.assert_array_equal(nl, nl2)
+        np.testing.assert_array_equal(kg, k2)
+        np.testing.assert_array_equal(vg, v2)

@@ -229,3 +229,34 @@ def test_batched_full_size_in_groups():
     loss_ref = num / (R * (B - 1))
     mean_w = float(np.sum(w[:, 1:].astype(np.float64))) / (R * (B - 1))
     assert abs(float(res.loss.cpu()[0]) - loss_ref) <= LOSS_W * mean_w + LOSS_REL * abs(loss_ref)
+
+
+def _sweep_cases(n=16, seed=3104):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        c = dict(R=int(rng.integers(1, 7)), B=int(rng.choice([1, 2, 9, 33, 64, 65, 128, 256])),
+                 H_extra=int(rng.integers(0, 3)),
+                 V=int(rng.choice([int(rng.integers(300, 5000)), int(rng.integers(5000, 40000)), 8192, 8193])),
+                 dtype="f32" if rng.random() < 0.4 else "bf16", scale=float(rng.choice([0.5, 3.0, 8.0])),
+                 wmode=str(rng.choice(["uniform", "zeros"])))
+        if c["R"] * (16 + c["H_extra"]) * c["V"] > 4_000_000:
+            continue
+        c["seed"] = int(rng.integers(1, 1 << 30))
+        cases.append(c)
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"sweep{i}" for i in range(len(SWEEP))])
+def test_exit_loss_sweep(case):
+    GP.log(f"[exit_loss] {case}")
+    zs, parents, tokens, w = _random_case(**case)
+    dtype = case["dtype"]
+    ref = oracle.exit_loss(zs, dtype, parents, tokens, w)
+    res = _gpu(zs, dtype, parents, tokens, w)
+    _compare(res, ref, parents, tokens, w)
+    flags = tev.tev_read_device_status(res.workspace, 3, parents.shape[0], parents.shape[1], zs.shape[-1])
+    assert not np.any(flags)

@@ -88,3 +88,31 @@ def test_predraw_flags_invalid_requests():
     torch.cuda.synchronize()
     assert np.all(nd[1].cpu().numpy() == -1) and np.all(en[1].cpu().numpy() == -1)
     assert np.all(en[0].cpu().numpy() >= 0)
+
+
+def _sweep_cases(n=16, seed=3102):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        R = int(rng.integers(1, 7))
+        B = int(rng.choice([1, 2, 9, 33, 64, 65, 128]))
+        V = int(rng.choice([int(rng.integers(500, 5000)), int(rng.integers(5000, 40000)), 4097, 8191]))
+        tree = str(rng.choice(["random", "chain", "star", "best_first"] if B >= 3 else ["random"]))
+        dtype = "f32" if rng.random() < 0.3 else "bf16"
+        if R * B * V > 8_000_000:
+            continue
+        cases.append(dict(name=f"sweep{len(cases)}", R=R, B=B, V=V, tree=tree, dtype=dtype,
+                          seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[c["name"] for c in SWEEP])
+def test_predraw_sweep(case):
+    c = dict(case)
+    name = c.pop("name")
+    GP.log(f"[predraw] {name} {c}")
+    wl = W.make_custom(name, with_attention=False, n_uniform=1, **c)
+    _check(wl, n=16, seed=c["seed"])
