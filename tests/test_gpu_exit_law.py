@@ -152,3 +152,42 @@ def test_workspace_reuse_across_calls():
         ok = ~(dr.band_exit | dr.band_bonus)
         assert np.array_equal(en.cpu().numpy()[ok], dr.exit_node[ok])
         assert np.array_equal(bt.cpu().numpy()[ok], dr.bonus_token[ok])
+
+
+def _value_cases(n=16, seed=3105):
+    """Seeded value ranges: logit spread from nearly flat to a few tokens
+    holding all the mass, drafted children boosted or not, temperatures
+    either side of 1, and one row with a single finite logit."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append(dict(name=f"values{i}", R=int(rng.integers(1, 5)),
+                          B=int(rng.choice([2, 9, 33, 64, 128])),
+                          V=int(rng.choice([int(rng.integers(100, 4096)), int(rng.integers(4096, 30000)), 8192])),
+                          dtype="f32" if rng.random() < 0.4 else "bf16",
+                          tree=str(rng.choice(["random", "chain", "star", "best_first"])),
+                          logit_sigma=float(rng.choice([0.1, 1.0, 3.0, 20.0, 60.0])),
+                          child_boost=float(rng.choice([0.0, 4.0, 20.0])),
+                          inv_temperature=float(rng.choice([0.25, 0.6, 1.0, 1.9])),
+                          seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+VALUES = _value_cases()
+
+
+@pytest.mark.parametrize("case", VALUES, ids=[c["name"] for c in VALUES])
+def test_value_sweep(case):
+    c = dict(case)
+    name = c.pop("name")
+    GP.log(f"[exit-law] {name} {c}")
+    wl = W.make_custom(name, with_attention=False, n_uniform=1024, **c)
+    # one node's row keeps a single finite logit (a one-hot target row)
+    lg = wl.logits.astype(np.float32) if wl.dtype == "f32" else W.bf16_bits_to_f32(wl.logits)
+    rng = np.random.default_rng(c["seed"])
+    r, v = int(rng.integers(0, wl.R)), int(rng.integers(0, wl.B))
+    keep = int(rng.integers(0, wl.V))
+    lg[r, v, :] = np.where(np.arange(wl.V) == keep, lg[r, v, keep], -np.inf)
+    wl.logits = lg if wl.dtype == "f32" else W.f32_to_bf16_bits(lg)
+    rep = GP.check_exit_law_and_draws(wl)
+    GP.log(f"[exit-law] {name} ok {rep}")
