@@ -31,7 +31,12 @@
 //               maximum over the key words, exact stages among the slots
 //               that tie there, one read of the winner's record, and the
 //               winner's slot moved to the next sibling and the new node's
-//               slot opened with its rank-0 child.
+//               slot opened with its rank-0 child.  With several draft modes
+//               the grid is R * M and each mode's pops go to a stream.
+//   k_tb_merge  grid R, 1024 threads (several modes only): the merged heap
+//               from the modes' streams -- each entry's place in the merged
+//               order, canonical prefix ids, the nodes at each prefix's
+//               first place.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
