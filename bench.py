@@ -585,11 +585,18 @@ def device_peaks():
     copy_s = t(lambda: dst.copy_(src), 10)
     read_s = t(lambda: f.sum(), 10)
     gemm_s = t(lambda: torch.matmul(a, b), 10)
+    # the qwen3_4b logit bytes (64 x 151936 bf16): a read of that size alone,
+    # over 16 distinct copies so that every read comes from HBM
+    small = src[: 16 * (64 * 151936 * 2)].view(torch.bfloat16).view(16, 64 * 151936)
+    ring = iter(range(1 << 30))
+    small_s = t(lambda: small[next(ring) % 16].sum(dtype=torch.float32), 160)
     out = {"copy_1gib_gbs": round(2 * n / copy_s / 1e9, 1), "read_1gib_gbs": round(n / read_s / 1e9, 1),
+           "read_qwen3_4b_logits_gbs": round(64 * 151936 * 2 / small_s / 1e9, 1),
            "gemm_bf16_8192_tflops": round(2 * 8192 ** 3 / gemm_s / 1e12, 1),
-           "note": "torch copy_ (bytes read + written), torch sum of f32 (bytes read), torch.matmul bf16; "
-                   "context for the 8 TB/s and 2.5 PFLOP/s spec peaks"}
-    del src, dst, a, b
+           "note": "torch copy_ (bytes read + written), torch sum of f32 (bytes read), torch sum of one "
+                   "19.45 MB bf16 tensor of 16 (the qwen3_4b logit bytes; launch gaps included), "
+                   "torch.matmul bf16; context for the 8 TB/s and 2.5 PFLOP/s spec peaks"}
+    del src, dst, a, b, small
     torch.cuda.empty_cache()
     return out
 
