@@ -237,17 +237,31 @@ def summarize_pmc(config: str, dbs):
     the L2's read requests and misses."""
     import sqlite3
     from collections import defaultdict
-    acc = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
+    # per database: a counter's rows of one dispatch (one per XCD or shader
+    # engine) are summed, then averaged over the dispatches; a counter that
+    # several passes collect (GRBM_GUI_ACTIVE, say) is averaged over them
+    per_db = []
     for db in dbs:
+        acc = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
         con = sqlite3.connect(db)
         for name, disp, ctr, val in con.execute(
                 "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
             acc[name][ctr][disp] += val
+        per_db.append(acc)
+
+    def combine(reduce_dispatches):
+        vals = defaultdict(lambda: defaultdict(list))
+        for acc in per_db:
+            for k, cs in acc.items():
+                for c, d in cs.items():
+                    vals[k][c].append(reduce_dispatches(list(d.values())))
+        return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+
     short = lambda k: k.replace("void ", "").replace("tev::(anonymous namespace)::", "").split("(")[0]
-    mean = {k: {c: sum(d.values()) / len(d) for c, d in cs.items()} for k, cs in acc.items()}
+    mean = combine(lambda v: sum(v) / len(v))
     # the calibration copy is the largest dispatch of the copy kernel (the
     # same kernel also moves the run's small inputs)
-    peak = {k: {c: max(d.values()) for c, d in cs.items()} for k, cs in acc.items()}
+    peak = combine(max)
     copy_k = max((k for k in peak if "copy" in k.lower()), key=lambda k: peak[k].get("FETCH_SIZE", 0.0),
                  default=None)
     cal = peak.get(copy_k, {}) if copy_k else {}
@@ -270,6 +284,15 @@ def summarize_pmc(config: str, dbs):
             d["mfma_flop"] = mops * 512
         if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in c:
             d["lds_read_bytes"] = c["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64
+        if c.get("SQ_WAVE_CYCLES"):
+            # shares of the waves' resident cycles (all in quad-cycles):
+            # waiting on a dependency (s_waitcnt, barrier), waiting to issue
+            # (the unit or the issue slot taken), issuing
+            wc = c["SQ_WAVE_CYCLES"]
+            d["wave_state"] = {n: c[f"SQ_{n.upper()}"] / wc for n in
+                               ("wait_any", "wait_inst_any", "active_inst_any", "active_inst_valu",
+                                "active_inst_lds", "active_inst_vmem", "wait_inst_lds")
+                               if f"SQ_{n.upper()}" in c}
         if "FETCH_SIZE" in c and cal.get("FETCH_SIZE"):
             d["fetch_bytes"] = c["FETCH_SIZE"] * COPY_BYTES / cal["FETCH_SIZE"]
         if "WRITE_SIZE" in c and cal.get("WRITE_SIZE"):

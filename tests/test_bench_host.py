@@ -119,6 +119,33 @@ def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     assert k["fetch_bytes"] == pytest.approx(2000.0 * b.COPY_BYTES / half_kib)
 
 
+def test_summarize_pmc_averages_a_counter_over_the_passes(tmp_path, monkeypatch):
+    b = _bench()
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    os.makedirs(tmp_path / "profiles")
+    kern = "void tev::(anonymous namespace)::k_demo<1>(int)"
+    # two passes of the same run, dispatch ids restarting at 1 in each; each
+    # collects GRBM_GUI_ACTIVE (two rows per dispatch, one per XCD group),
+    # which must be summed within a pass and averaged over the passes
+    sq = [(kern, 1, "GRBM_GUI_ACTIVE", 4 * 900.0), (kern, 1, "GRBM_GUI_ACTIVE", 4 * 900.0),
+          (kern, 1, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 450.0)]
+    wave = [(kern, 1, "GRBM_GUI_ACTIVE", 4 * 1100.0), (kern, 1, "GRBM_GUI_ACTIVE", 4 * 1100.0),
+            (kern, 1, "SQ_WAVE_CYCLES", 200.0), (kern, 1, "SQ_WAIT_ANY", 50.0),
+            (kern, 1, "SQ_WAIT_INST_ANY", 30.0), (kern, 1, "SQ_ACTIVE_INST_ANY", 120.0)]
+    dbs = [str(tmp_path / "sq.db"), str(tmp_path / "wave.db")]
+    _pmc_db(dbs[0], sq)
+    _pmc_db(dbs[1], wave)
+    b.summarize_pmc("demo", dbs)
+    k = json.load(open(tmp_path / "profiles" / "pmc_demo.json"))["kernels"]["k_demo<1>"]
+    assert k["cycles"] == pytest.approx(1000.0)        # (900 + 1100) / 2, not their sum
+    assert k["mfma_busy_frac"] == pytest.approx(0.45)
+    ws = k["wave_state"]
+    assert ws["wait_any"] == pytest.approx(0.25)
+    assert ws["wait_inst_any"] == pytest.approx(0.15)
+    assert ws["active_inst_any"] == pytest.approx(0.6)
+    assert "active_inst_lds" not in ws                # not collected
+
+
 def test_traffic_is_dropped_when_the_sources_changed(tmp_path, monkeypatch):
     b = _bench()
     monkeypatch.setattr(b, "ROOT", str(tmp_path))
